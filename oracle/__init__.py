@@ -1,0 +1,16 @@
+"""CPU oracle for attention over a paged KV cache (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP library.
+"""
+from .paged_attention import (  # noqa: F401
+    combine,
+    decode,
+    decode_partials,
+    extend,
+    gather,
+    kv_store,
+    round_to_bf16_f64,
+    token_slots,
+    widen,
+)

@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+One step = one decode layer-step of the Qwen3-8B-shaped batch with radix
+prefix sharing (256 requests, log-uniform lengths 512..8192, 32 query / 8 KV
+heads, head_dim 128, page 16, bf16): kv_store of the 256 new K/V rows, then
+paged decode (partial kernel + combine kernel).  Inputs are resident in HBM
+before timing starts.  The chunked-prefill extend call (8 requests, prefix
+0..4096 + 512-token chunk, same head shape) is timed in the same run and
+reported in its own object.
+
+Prints one JSON line.  `value` is decode KV throughput in GB/s counted on the
+distinct KV bytes the step must read (each physical slot once); `roofline`
+describes the dominant kernel (the decode partial kernel) with its average
+duration taken from HIP events on the launch stream; `cpu_baseline` is the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_partial_qwen3_8b_radix_counters.txt")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_attention_11_amd", "csrc", f)
+                  for f in ("decode.hip", "device.h", "internal.h")]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen3_8b_radix")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extend", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU leg")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def sources_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(launch_units):
+    """HBM bytes per partial-kernel launch from the committed counter summary,
+    if it was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    kv = {}
+    for line in open(PROFILE_COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != sources_digest(DECODE_SOURCES):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping)
+    order = np.random.default_rng(0).permutation(wl.num_seqs)
+    done, t_used, nbytes = 0, 0.0, 0
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    while done < wl.num_seqs and t_used < target_s:
+        k = 4 if done == 0 else max(1, min(wl.num_seqs - done, int(done * (target_s - t_used) / max(t_used, 1e-3))))
+        seqs = order[done:done + k]
+        sub = wl.subset(seqs)
+        t0 = time.perf_counter()
+        oracle.decode(sub.q, kp, vp, sub.page_table, sub.seq_lens, wl.scale, wl.dtype)
+        t_used += time.perf_counter() - t0
+        nbytes += int(sub.seq_lens.sum()) * per_tok
+        done += k
+    return {
+        "value": round(nbytes / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle.decode (float64 numpy) over {done} of {wl.num_seqs} requests of the same workload "
+                  f"({nbytes / 1e9:.3f} GB of K/V read, logical), {t_used:.1f} s; store excluded; "
+                  f"host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(attention shards over KV heads with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_11_amd as pa
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    pa.load()
+    dev_name = torch.cuda.get_device_name(0)
+
+    # ---------------- decode step: store + partial + combine
+    t0 = time.perf_counter()
+    wl = W.make(args.config)
+    log(f"generated {args.config} in {time.perf_counter() - t0:.1f}s")
+    dw = W.to_device(wl)
+    B, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    split = args.split_tokens or pa.decode_split_tokens(B, Hkv, wl.max_seq_len)
+    out = torch.empty_like(dw.q)
+    ws = pa.decode_workspace(dw.q, dw.k_pool, wl.max_seq_len, split)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        pa.kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.decode_partial(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, wl.scale,
+                          out, ws, split)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.decode_combine(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, wl.scale,
+                          out, ws, split)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log(f"decode: {ms_step * 1e3:.1f} us/step, partial {partial_ms * 1e3:.1f} us (wall {wall:.3f}s)")
+
+    kv_unique = wl.kv_bytes_unique()
+    kv_logical = wl.kv_bytes_logical()
+    P = wl.page_size
+    pt_bytes = 4 * int(sum((int(L) + P - 1) // P for L in wl.seq_lens))
+    q_bytes = B * Hq * D * wl.elem_bytes
+    partial_alg_bytes = kv_unique + q_bytes + pt_bytes + 4 * B  # per partial launch
+    achieved = partial_alg_bytes / (partial_ms * 1e-3) / 1e9
+    traffic = read_traffic(1)
+    value = kv_unique / (ms_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "paged-attn decode KV HBM GB/s (% of peak) + decode tokens/s, Qwen3-8B shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.config,
+            "description": W.DESCRIPTIONS.get(args.config, args.config),
+            "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
+            "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "split_tokens": split,
+            "step": "kv_store + decode_partial + decode_combine",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "kv_bytes_unique": kv_unique,
+        "kv_bytes_logical": kv_logical,
+        "logical_kv_GBps": round(kv_logical / (ms_step * 1e-3) / 1e9, 2),
+        "partial_kernel_us": round(partial_ms * 1e3, 2),
+        "roofline": {
+            "kernel": "decode_partial_kernel<bf16, D=128, G=4>",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": partial_alg_bytes,
+        },
+        "device": dev_name,
+    }
+
+    # ---------------- extend (chunked prefill on the same head shape)
+    if not args.no_extend:
+        del ws
+        ew = W.make("qwen3_8b_extend")
+        edw = W.to_device(ew)
+        eout = torch.empty_like(edw.q)
+        pa.kv_store(edw.k_pool, edw.v_pool, edw.k_new, edw.v_new, edw.slot_mapping)
+
+        def ext():
+            pa.extend(edw.q, edw.q_indptr, edw.k_pool, edw.v_pool, edw.page_table, edw.seq_lens, ew.max_q_len,
+                      ew.max_seq_len, ew.scale, out=eout)
+
+        for _ in range(max(3, args.warmup // 2)):
+            ext()
+        torch.cuda.synchronize()
+        es, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ksteps = max(5, args.steps // 2)
+        es.record(stream)
+        for _ in range(ksteps):
+            ext()
+        ee.record(stream)
+        torch.cuda.synchronize()
+        ems = es.elapsed_time(ee) / ksteps
+        n = ew.n_new.astype(np.int64)
+        p = (ew.seq_lens - ew.n_new).astype(np.int64)
+        flops = 4 * ew.head_dim * ew.num_q_heads * int(np.sum(n * p + n * (n + 1) // 2))
+        tf = flops / (ems * 1e-3) / 1e12
+        result["extend"] = {
+            "workload": "qwen3_8b_extend",
+            "description": W.DESCRIPTIONS["qwen3_8b_extend"],
+            "kernel_us": round(ems * 1e3, 2),
+            "tokens_per_s": round(int(n.sum()) / (ems * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": flops},
+        }
+        log(f"extend: {ems * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+
+    # ---------------- CPU oracle on a bounded sample (rank 0, N=1 only)
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']['value']} GB/s in {time.perf_counter() - t0:.1f}s")
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

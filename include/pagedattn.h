@@ -1,0 +1,197 @@
+/*
+ * pagedattn.h -- C ABI of a gfx950 (MI355X) library for attention over a
+ * paged KV cache.
+ *
+ * The operations are the hot path of the small SGLang-style serving engines
+ * described on the pages (nanoSGLang README, mini-sglang README, nanollmserve
+ * README, "mini-sglang from Scratch", Mini-SGLang README of the yangyonggit
+ * fork):
+ *
+ *   pa_kv_store    write a step's new K/V rows into the pool slots given by a
+ *                  slot mapping ("mini-sglang from Scratch", section "How this
+ *                  book works": the KV-cache writes);
+ *   pa_decode      one new token per request attends every cached key of its
+ *                  request through the page table, grouped-query heads
+ *                  (Mini-SGLang README, section Reference Attention Backends;
+ *                  nanoSGLang README, section Ablation: zero-copy paged
+ *                  attention through page-table indirection);
+ *   pa_extend      a chunk of new tokens per request (chunked prefill, or the
+ *                  parallel verification of drafted tokens) attends the cached
+ *                  prefix and, causally, the chunk itself (Mini-SGLang README,
+ *                  sections Reference Attention Backends and Speculative
+ *                  Decoding; nanollmserve README, section v0.7 Chunked
+ *                  Prefill);
+ *   pa_gather      copy requests' pages out to contiguous K/V (test and
+ *                  calibration helper: the legacy per-token copy that paged
+ *                  attention removes, nanoSGLang README, section Ablation).
+ *
+ * Data layout (all device memory, owned by the caller):
+ *   k_pool, v_pool  [num_pages, page_size, num_kv_heads, head_dim], contiguous
+ *                   ("NHD", nanoSGLang README, section Architecture).  Token
+ *                   t of a request lives in physical page page_table[t /
+ *                   page_size] at offset t % page_size; its flat slot is
+ *                   page * page_size + offset.
+ *   page_table      int32 [num_seqs, pt_stride], row-major.  Entries at or
+ *                   beyond ceil(seq_len / page_size) are never read.
+ *   seq_lens        int32 [num_seqs]: keys of each request *including* the
+ *                   new tokens, which must already have been stored.
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless stated otherwise; `stream` is a
+ *     hipStream_t (NULL = the default stream).  Every call only enqueues work
+ *     on `stream` and returns; none synchronises, allocates or frees memory,
+ *     so the calls can be captured into a HIP graph.
+ *   - Scalars and pointers are validated on the host before any HIP call; a
+ *     call that returns an error has launched nothing.  PA_ERR_HIP reports a
+ *     launch failure (hipGetLastError after the launch).
+ *   - Values that live in device memory (page ids, seq_lens, slot mapping,
+ *     q_indptr) are a caller contract and are not checked: page ids must be in
+ *     [0, num_pages), seq_lens in [0, max_seq_len], slots in
+ *     [0, num_pages * page_size) or negative (skip), distinct.
+ *   - The library keeps no state between calls and is thread-safe.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  PA_ERR_SHAPE = 2,       /* sizes are negative or inconsistent                 */
+  PA_ERR_DTYPE = 3,       /* unknown dtype, or a dtype this call does not take  */
+  PA_ERR_UNSUPPORTED = 4, /* valid, but head_dim / group / page size not built  */
+  PA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned         */
+  PA_ERR_HIP = 6          /* a HIP runtime call reported an error               */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* A paged K/V pool in caller-owned device memory. */
+typedef struct {
+  void* k_pool;         /* [num_pages, page_size, num_kv_heads, head_dim]     */
+  void* v_pool;         /* same shape and dtype                               */
+  int64_t num_pages;    /* > 0; num_pages * page_size must be < 2^31          */
+  int32_t page_size;    /* power of two, 1 .. 256                             */
+  int32_t num_kv_heads; /* >= 1                                               */
+  int32_t head_dim;     /* 64 or 128                                          */
+  int32_t dtype;        /* pa_dtype; elements of K, V, q and out              */
+} pa_kv_pool;
+
+/* Library version string (static storage). */
+const char* pa_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(int32_t status);
+
+/*
+ * pa_kv_store: for each i in [0, num_rows) with slot_mapping[i] >= 0, copy row
+ * k_new[i] ([num_kv_heads, head_dim], pool dtype) to flat slot
+ * slot_mapping[i] of k_pool, and v_new[i] to the same slot of v_pool.  A byte
+ * copy: bit-exact, no conversion.  Negative slots are padding and are skipped
+ * (fixed-size buffers can be reused).  k_new, v_new: [num_rows, num_kv_heads,
+ * head_dim] contiguous, 16-byte aligned.  num_rows == 0 is a no-op.
+ * Overlapping slots are undefined.
+ */
+pa_status pa_kv_store(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int64_t num_rows, void* stream);
+
+/*
+ * Decode split plan.  The key range of each request is cut into consecutive
+ * pieces of split_tokens keys; each (request, KV head, piece) is one unit of
+ * work, and a second kernel merges the pieces by log-sum-exp weights.
+ * pa_decode_split_tokens returns the piece length the library chooses from
+ * the host-side sizes alone (a multiple of 64, at most 1024).  Every decode
+ * call takes a split_tokens argument: 0 means "this automatic choice", any
+ * other value must be a multiple of 64 in [64, 1024].  The result depends on
+ * the split only through floating-point rounding.
+ */
+int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes and split_tokens
+ * (0 = the automatic plan); 0 on invalid sizes.  Layout:
+ * fp32 partial outputs [num_seqs, num_q_heads, S, head_dim] followed (at a
+ * 256-byte boundary) by fp32 log2-sum-exp values [num_seqs, num_q_heads, S],
+ * S = ceil(max_seq_len / split_tokens).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t split_tokens);
+
+/*
+ * pa_decode: out[b, h, :] = softmax(scale * K_b,g q[b, h, :]) V_b,g over the
+ * seq_lens[b] keys of request b, g = h / (num_q_heads / num_kv_heads).
+ *   q     [num_seqs, num_q_heads, head_dim], pool dtype, 16-byte aligned
+ *   out   [num_seqs, num_q_heads, head_dim], pool dtype (bf16 outputs are
+ *         rounded once, to nearest even, from fp32 accumulation)
+ *   page_table [num_seqs, pt_stride]; pt_stride * page_size >= max_seq_len
+ *   max_seq_len: host-side upper bound of seq_lens (sizes the grid; no
+ *         device read)
+ *   workspace: >= pa_decode_workspace_bytes(...) bytes, 256-byte aligned;
+ *         its contents need no initialisation and are clobbered.
+ * A request with seq_len 0 gets a zero row.  Requires num_q_heads a multiple
+ * of num_kv_heads with group size 1..8 (fp32: group * head_dim <= 512).
+ * Enqueues pa_decode_partial then pa_decode_combine.
+ */
+pa_status pa_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two kernels of pa_decode, callable one at a time (same arguments).
+ * pa_decode_partial writes, for every request with more than one piece, the
+ * normalised output and log2-sum-exp of each piece into the workspace, and
+ * writes `out` directly for requests with exactly one piece.
+ * pa_decode_combine merges the pieces into `out` for requests with more than
+ * one piece and writes zero rows for requests with seq_len 0.
+ */
+pa_status pa_decode_partial(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_combine(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_extend: request b has n_b = q_indptr[b+1] - q_indptr[b] new tokens
+ * whose K/V rows are already stored, after a cached prefix of
+ * p_b = seq_lens[b] - n_b keys.  Its new token i (absolute position p_b + i)
+ * attends keys 0 .. p_b + i:
+ *   out[q_indptr[b] + i, h, :] = softmax(scale * K q) V over those keys.
+ *   q, out     [q_indptr[num_seqs], num_q_heads, head_dim], bf16, 16-byte
+ *              aligned; q_indptr int32 [num_seqs + 1], non-decreasing
+ *   max_q_len  host-side upper bound of n_b; max_seq_len of seq_lens.
+ * bf16 pools only, head_dim 128 or 64, group size 1, 2, 4 or 8.  Scores and
+ * the output are accumulated in fp32; softmax weights are rounded to bf16
+ * before the weighted sum of V (matrix-core inputs).
+ */
+pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                    const int32_t* q_indptr, const int32_t* page_table, int32_t pt_stride,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t max_q_len,
+                    int32_t max_seq_len, float scale, void* out, void* stream);
+
+/*
+ * pa_gather: copy the first seq_lens[b] tokens of every request, in logical
+ * order, to contiguous k_out / v_out rows starting at row out_offsets[b]
+ * (int64 [num_seqs + 1], device).  k_out, v_out: [out_offsets[num_seqs],
+ * num_kv_heads, head_dim], pool dtype.  Bit-exact.  Test and calibration
+ * helper.
+ */
+pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                    const int32_t* seq_lens, const int64_t* out_offsets, int32_t num_seqs,
+                    int32_t max_seq_len, void* k_out, void* v_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,268 @@
+"""Python binding of libpagedattn.so (gfx950 paged KV-cache attention).
+
+Argument marshalling only: every function passes torch tensors' device
+pointers and the current HIP stream to the C ABI declared in
+include/pagedattn.h, and raises PagedAttnError on a non-zero status.  All
+computation happens in the library's HIP kernels; there is no fallback.  If
+the shared library has not been built, the first call raises.
+
+Tensors:
+  k_pool, v_pool  [num_pages, page_size, num_kv_heads, head_dim], bf16 or fp32,
+                  contiguous, on the GPU
+  page_table      int32 [num_seqs, stride];  seq_lens int32 [num_seqs]
+  slot_mapping    int64 [num_rows];  q_indptr int32 [num_seqs + 1]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+from typing import Optional
+
+__all__ = [
+    "PagedAttnError", "library_path", "load", "version", "kv_store", "decode", "decode_partial",
+    "decode_combine", "decode_split_tokens", "decode_workspace_bytes", "extend", "gather",
+]
+
+_PKG = Path(__file__).resolve().parent
+_LIB_NAME = "libpagedattn.so"
+
+PA_F32, PA_BF16 = 0, 1
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
+                4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().pa_status_string(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({msg})")
+
+
+class KVPool(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
+        ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_POOLP = ctypes.POINTER(KVPool)
+_DECODE_ARGS = [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]
+
+SIGNATURES = {
+    # name: (restype, argtypes) -- mirrors include/pagedattn.h
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_status_string": (ctypes.c_char_p, [_i32]),
+    "pa_kv_store": (_i32, [_POOLP, _vp, _vp, _vp, _i64, _vp]),
+    "pa_decode_split_tokens": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, _DECODE_ARGS),
+    "pa_decode_partial": (_i32, _DECODE_ARGS),
+    "pa_decode_combine": (_i32, _DECODE_ARGS),
+    "pa_extend": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp]),
+    "pa_gather": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
+}
+
+
+def library_path() -> Path:
+    return Path(os.environ.get("PAGEDATTN_LIB", _PKG / _LIB_NAME))
+
+
+def load() -> ctypes.CDLL:
+    """Load the shared library (once) and declare its signatures."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not path.exists():
+            raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_attention_11_amd.build`")
+        lib = ctypes.CDLL(str(path))
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+_lib = load
+
+
+def version() -> str:
+    return load().pa_version().decode()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PagedAttnError(status, where)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_pool(k_pool, v_pool) -> KVPool:
+    torch = _torch()
+    if k_pool.shape != v_pool.shape or k_pool.dtype != v_pool.dtype:
+        raise ValueError("k_pool and v_pool must have the same shape and dtype")
+    if k_pool.dim() != 4:
+        raise ValueError("pools are [num_pages, page_size, num_kv_heads, head_dim]")
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool")
+    dt = {torch.bfloat16: PA_BF16, torch.float32: PA_F32}.get(k_pool.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported pool dtype {k_pool.dtype}")
+    n, P, H, D = k_pool.shape
+    return KVPool(k_pool.data_ptr(), v_pool.data_ptr(), n, P, H, D, dt)
+
+
+# --------------------------------------------------------------------------
+# the calls
+# --------------------------------------------------------------------------
+def kv_store(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
+    """Write row i of k_new/v_new [N, H_kv, D] to flat slot slot_mapping[i]
+    (int64; negative = skip) of the pools, in place."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(k_new, "k_new", k_pool.dtype)
+    _dev(v_new, "v_new", k_pool.dtype)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    st = load().pa_kv_store(ctypes.byref(pool), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                            slot_mapping.numel(), _stream(stream))
+    _check(st, "pa_kv_store")
+
+
+def decode_split_tokens(num_seqs: int, num_kv_heads: int, max_seq_len: int) -> int:
+    return load().pa_decode_split_tokens(num_seqs, num_kv_heads, max_seq_len)
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, split_tokens=0) -> int:
+    return load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                            split_tokens)
+
+
+def decode_workspace(q, k_pool, max_seq_len, split_tokens=0):
+    """A workspace tensor of the right size for decode(...)."""
+    torch = _torch()
+    nbytes = decode_workspace_bytes(q.shape[0], q.shape[1], k_pool.shape[2], k_pool.shape[3], max_seq_len,
+                                    split_tokens)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+
+
+def _decode_call(fn_name, q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out, workspace,
+                 split_tokens, stream):
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(q, "q", k_pool.dtype)
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != k_pool.shape[3]:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    if page_table.dim() != 2 or page_table.shape[0] != q.shape[0] or seq_lens.numel() != q.shape[0]:
+        raise ValueError("page_table [num_seqs, stride] and seq_lens [num_seqs] must match q")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if workspace is None:
+        workspace = decode_workspace(q, k_pool, max_seq_len, split_tokens)
+    _dev(workspace, "workspace")
+    st = getattr(load(), fn_name)(
+        ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+        q.shape[0], int(max_seq_len), float(scale), int(split_tokens), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, fn_name)
+    return out
+
+
+def decode(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out=None, workspace=None,
+           split_tokens=0, stream=None):
+    """Paged decode attention: q [B, H_q, D] -> out [B, H_q, D] (pool dtype)."""
+    return _decode_call("pa_decode", q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out,
+                        workspace, split_tokens, stream)
+
+
+def decode_partial(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out, workspace,
+                   split_tokens=0, stream=None):
+    """First kernel of decode (per-piece partials; single-piece rows to out)."""
+    return _decode_call("pa_decode_partial", q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale,
+                        out, workspace, split_tokens, stream)
+
+
+def decode_combine(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out, workspace,
+                   split_tokens=0, stream=None):
+    """Second kernel of decode (merge pieces into out)."""
+    return _decode_call("pa_decode_combine", q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale,
+                        out, workspace, split_tokens, stream)
+
+
+def extend(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, max_seq_len, scale, out=None,
+           stream=None):
+    """Paged extend attention: q [T_q, H_q, D] bf16 -> out [T_q, H_q, D] bf16."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16)
+    _dev(q_indptr, "q_indptr", torch.int32)
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != k_pool.shape[3]:
+        raise ValueError("q must be [T_q, num_q_heads, head_dim]")
+    B = seq_lens.numel()
+    if q_indptr.numel() != B + 1 or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("q_indptr [B+1], page_table [B, stride], seq_lens [B] must agree")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    st = load().pa_extend(ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(q_indptr), _ptr(page_table),
+                          page_table.shape[1], _ptr(seq_lens), B, int(max_q_len), int(max_seq_len),
+                          float(scale), _ptr(out), _stream(stream))
+    _check(st, "pa_extend")
+    return out
+
+
+def gather(k_pool, v_pool, page_table, seq_lens, out_offsets, max_seq_len, k_out, v_out, stream=None):
+    """Copy each request's first seq_lens[b] tokens to rows out_offsets[b].. of
+    k_out / v_out [total, H_kv, D]."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(out_offsets, "out_offsets", torch.int64)
+    _dev(k_out, "k_out", k_pool.dtype)
+    _dev(v_out, "v_out", k_pool.dtype)
+    st = load().pa_gather(ctypes.byref(pool), _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                          _ptr(out_offsets), seq_lens.numel(), int(max_seq_len), _ptr(k_out), _ptr(v_out),
+                          _stream(stream))
+    _check(st, "pa_gather")

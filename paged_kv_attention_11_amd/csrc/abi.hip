@@ -1,0 +1,274 @@
+// C ABI of the paged-attention library: host-side validation and dispatch.
+// Every argument is checked before the first HIP call; a call that fails
+// validation launches nothing.  The library allocates nothing, never
+// synchronises, and keeps no state.
+#include <limits.h>
+
+#include "../../include/pagedattn.h"
+#include "internal.h"
+
+namespace {
+
+using pa::kMaxGroup;
+using pa::kMaxSplitTokens;
+using pa::kSplitQuantum;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Work-groups the automatic split plan aims for: about eight per compute unit
+// on a 256-CU device, enough to fill the chip and even out the tail.
+constexpr int64_t kTargetUnits = 2048;
+constexpr int kAutoMaxSplit = 512;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
+
+pa_status check_pool(const pa_kv_pool* pool) {
+  if (!pool) return PA_ERR_NULL;
+  if (pool->dtype != PA_F32 && pool->dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (pool->num_pages <= 0 || pool->page_size <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (!pool->k_pool || !pool->v_pool) return PA_ERR_NULL;
+  if ((pool->page_size & (pool->page_size - 1)) != 0 || pool->page_size > 256) return PA_ERR_UNSUPPORTED;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (pool->num_pages > (int64_t)INT_MAX / pool->page_size) return PA_ERR_SHAPE;
+  if (!aligned(pool->k_pool, 16) || !aligned(pool->v_pool, 16)) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+int32_t resolve_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len);
+
+int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return kSplitQuantum;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int64_t want = (kTargetUnits + units - 1) / units;  // pieces per request
+  int64_t split = (max_seq_len + want - 1) / want;
+  split = (split + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
+  if (split < kSplitQuantum) split = kSplitQuantum;
+  if (split > kAutoMaxSplit) split = kAutoMaxSplit;
+  return (int32_t)split;
+}
+
+bool valid_split(int32_t s) { return s >= kSplitQuantum && s <= kMaxSplitTokens && s % kSplitQuantum == 0; }
+
+int32_t resolve_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  if (split_tokens == 0) return auto_split(num_seqs, num_kv_heads, max_seq_len);
+  return valid_split(split_tokens) ? split_tokens : -1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                       int32_t split) {
+  const int64_t S = (max_seq_len + split - 1) / split;
+  const size_t rows = (size_t)num_seqs * num_q_heads * S;
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+// Shared validation of the three decode calls; fills `a` on success.
+pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                         const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                         int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
+                         void* out, void* workspace, size_t ws_bytes, pa::DecodeArgs& a) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || pt_stride < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (pool->dtype == PA_F32 && G * pool->head_dim > 512) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
+  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
+  if (split < 0) return PA_ERR_SHAPE;
+  const int64_t S = (max_seq_len + split - 1) / split;
+  if ((int64_t)num_seqs * pool->num_kv_heads * S > (int64_t)INT_MAX) return PA_ERR_SHAPE;
+  if (num_seqs > 0) {
+    if (!q || !page_table || !seq_lens || !out) return PA_ERR_NULL;
+    if (!aligned(q, 16)) return PA_ERR_SHAPE;
+    const size_t need = workspace_bytes(num_seqs, num_q_heads, pool->head_dim, max_seq_len, split);
+    if (ws_bytes < need) return PA_ERR_WORKSPACE;
+    if (S > 0 && (!workspace || !aligned(workspace, 256))) return PA_ERR_WORKSPACE;
+  }
+  const size_t rows = (size_t)num_seqs * num_q_heads * S;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.q = q;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.o_part = (float*)workspace;
+  a.lse = workspace ? (float*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float))) : nullptr;
+  a.out = out;
+  a.pt_stride = pt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.log2_page = ilog2(pool->page_size);
+  a.split_tokens = split;
+  a.max_splits = (int32_t)S;
+  a.bf16 = pool->dtype == PA_BF16;
+  a.scale_log2 = scale * kLog2e;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_version(void) { return "pagedattn 0.1.0 gfx950"; }
+
+const char* pa_status_string(int32_t s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_SHAPE: return "bad or inconsistent sizes";
+    case PA_ERR_DTYPE: return "unsupported dtype";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, group size or page size";
+    case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+pa_status pa_kv_store(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int64_t num_rows, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_rows < 0) return PA_ERR_SHAPE;
+  if (num_rows == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return PA_ERR_SHAPE;
+  pa::StoreArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.num_rows = num_rows;
+  a.row_chunks = pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype) / 16;
+  return hip_status(pa::launch_kv_store(a, (hipStream_t)stream));
+}
+
+int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  return auto_split(num_seqs, num_kv_heads, max_seq_len);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t split_tokens) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
+    return 0;
+  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
+  if (split < 0) return 0;
+  return workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, split);
+}
+
+pa_status pa_decode_partial(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
+                            void* out, void* workspace, size_t workspace_bytes_, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs,
+                                max_seq_len, scale, split_tokens, out, workspace, workspace_bytes_, a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return hip_status(pa::launch_decode_partial(a, (hipStream_t)stream));
+}
+
+pa_status pa_decode_combine(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
+                            void* out, void* workspace, size_t workspace_bytes_, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs,
+                                max_seq_len, scale, split_tokens, out, workspace, workspace_bytes_, a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return hip_status(pa::launch_decode_combine(a, (hipStream_t)stream));
+}
+
+pa_status pa_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* page_table,
+                    int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                    float scale, int32_t split_tokens, void* out, void* workspace,
+                    size_t workspace_bytes_, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs,
+                                max_seq_len, scale, split_tokens, out, workspace, workspace_bytes_, a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  st = hip_status(pa::launch_decode_partial(a, (hipStream_t)stream));
+  if (st != PA_OK) return st;
+  return hip_status(pa::launch_decode_combine(a, (hipStream_t)stream));
+}
+
+pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* q_indptr,
+                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t max_q_len, int32_t max_seq_len, float scale, void* out,
+                    void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || max_q_len < 0 || max_seq_len < 0 || pt_stride < 0 || num_q_heads <= 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (max_q_len > max_seq_len) return PA_ERR_SHAPE;
+  if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
+  const int64_t qblocks = (max_q_len + 128 / G - 1) / (128 / G);
+  if (qblocks * pool->num_kv_heads * num_seqs > (int64_t)INT_MAX) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (!q || !q_indptr || !page_table || !seq_lens || !out) return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return PA_ERR_SHAPE;
+  pa::ExtendArgs a;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.q = q;
+  a.q_indptr = q_indptr;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.pt_stride = pt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.log2_page = ilog2(pool->page_size);
+  a.max_q_len = max_q_len;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(pa::launch_extend(a, (hipStream_t)stream));
+}
+
+pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                    const int32_t* seq_lens, const int64_t* out_offsets, int32_t num_seqs,
+                    int32_t max_seq_len, void* k_out, void* v_out, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || pt_stride < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_seq_len == 0) return PA_OK;
+  if (!page_table || !seq_lens || !out_offsets || !k_out || !v_out) return PA_ERR_NULL;
+  if (!aligned(k_out, 16) || !aligned(v_out, 16)) return PA_ERR_SHAPE;
+  pa::GatherArgs a;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.out_offsets = out_offsets;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.pt_stride = pt_stride;
+  a.num_seqs = num_seqs;
+  a.max_seq_len = max_seq_len;
+  a.log2_page = ilog2(pool->page_size);
+  a.row_chunks = pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype) / 16;
+  return hip_status(pa::launch_gather(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,431 @@
+// Paged decode attention for gfx950: one new query token per request attends
+// every key of its request through the page table, with grouped-query heads.
+//
+// What is computed (Mini-SGLang README, yangyonggit fork, section Reference
+// Attention Backends: paged gather, GQA by repeat_interleave; nanoSGLang
+// README, section Ablation: attention straight from the pages through the
+// page table, no per-token copy):
+//   out[b,h] = softmax(scale * K_{b,g} q[b,h]) V_{b,g},  g = h / G.
+// The triton backend on the same page runs an online (FlashAttention-style)
+// softmax per (request, head); this design keeps the online softmax but
+// reorganises the work for an HBM-bound gfx950 kernel:
+//
+//  * Split-K over keys.  Work unit = (request b, KV head g, piece s of
+//    split_tokens keys).  decode_partial_kernel writes the piece's
+//    normalised output o_s and its log2-sum-exp; decode_combine_kernel merges
+//    pieces with weights 2^(lse_s - max lse).  A request with one piece is
+//    finished by the partial kernel directly.
+//  * GQA sharing.  A work-group serves all G query heads of KV head g, so
+//    every K/V byte is fetched from HBM once per work unit and reused G times
+//    from registers.
+//  * Loads.  Each wave takes 16 keys per iteration.  K is read in a
+//    "quad" layout: four lanes per key, lane c holding 16-byte pieces
+//    c, c+4, ... of the key's head row; the QK dot product is a packed bf16
+//    dot (v_dot2_f32_bf16) plus a two-step DPP quad reduction.  V is read in
+//    a "row" layout: D/8 consecutive lanes cover one key's head row with
+//    16-byte loads, so each load instruction covers whole cache lines.
+//    Softmax weights move from the K layout to the V layout through LDS.
+//  * Online softmax with a wave-uniform reference maximum.  The reference is
+//    raised (and the accumulator rescaled) only when a score exceeds it by
+//    more than 2^8 in the exponent, so the common iteration does no cross-lane
+//    maximum and no rescale; the result is exact because numerator and
+//    denominator carry the same reference.
+//  * Key slots of the piece (page_table[t / P] * P + t % P) are computed once
+//    per work-group into LDS.
+#include <type_traits>
+
+#include "device.h"
+#include "internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kThreads = kDecodeWaves * 64;
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+template <bool BF16, int D, int G>
+struct DecodeCfg {
+  static constexpr int EPC = BF16 ? 8 : 4;        // elements per 16-byte piece
+  static constexpr int CPR = D / EPC;              // pieces per head row
+  static constexpr int NK = CPR / 4;               // K pieces per lane (quad layout)
+  static constexpr int LPR = CPR;                  // lanes per V row
+  static constexpr int RPI = 64 / LPR;             // V rows per load instruction
+  static constexpr int NV = kDecodeTokPerIter / RPI;  // V pieces per lane per iteration
+  static constexpr int GP = (G + 3) & ~3;          // group padded for float4 LDS reads
+  static_assert(NK >= 1 && RPI >= 1 && NV >= 1, "bad tiling");
+};
+
+template <bool BF16, int D, int G>
+struct Tile {
+  using C = DecodeCfg<BF16, D, G>;
+  uint4 k[C::NK];
+  uint4 v[C::NV];
+};
+
+// QK partial dot product of one 16-byte piece.
+template <bool BF16>
+__device__ __forceinline__ float dot_piece(const uint4& q, const uint4& k, float acc) {
+  if constexpr (BF16) {
+    acc = dot2_bf16(q.x, k.x, acc);
+    acc = dot2_bf16(q.y, k.y, acc);
+    acc = dot2_bf16(q.z, k.z, acc);
+    acc = dot2_bf16(q.w, k.w, acc);
+  } else {
+    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  }
+  return acc;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen_piece(const uint4& v, float* f) {
+  if constexpr (BF16) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  } else {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+}
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeArgs p) {
+  using C = DecodeCfg<BF16, D, G>;
+  using T = std::conditional_t<BF16, uint16_t, float>;
+  constexpr int EPC = C::EPC, NK = C::NK, NV = C::NV, RPI = C::RPI, LPR = C::LPR, GP = C::GP;
+
+  __shared__ int32_t s_slot[kMaxSplitTokens];
+  __shared__ float4 s_p4[kDecodeWaves][kDecodeTokPerIter][GP / 4];
+  __shared__ float s_acc[kDecodeWaves][G][D];
+  __shared__ float s_m[kDecodeWaves][G];
+  __shared__ float s_l[kDecodeWaves][G];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  int bid = blockIdx.x;
+  const int S = p.max_splits;
+  const int s = bid % S;
+  bid /= S;
+  const int g = bid % p.num_kv_heads;
+  const int b = bid / p.num_kv_heads;
+
+  const int L = p.seq_lens[b];
+  const int t_begin = s * p.split_tokens;
+  if (t_begin >= L) return;  // uniform over the work-group
+  const int n_tok = min(L - t_begin, p.split_tokens);
+  const int n_splits = (L + p.split_tokens - 1) / p.split_tokens;
+
+  // ---- stage the piece's key slots in LDS
+  {
+    const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride;
+    const int sh = p.log2_page;
+    const int pmask = (1 << sh) - 1;
+    for (int i = tid; i < n_tok; i += kThreads) {
+      const int t = t_begin + i;
+      s_slot[i] = (pt[t >> sh] << sh) | (t & pmask);
+    }
+  }
+
+  // ---- the group's queries, quad layout: lane c holds pieces c, c+4, ...
+  const int c = lane & 3;
+  const int tq = lane >> 2;  // key within the iteration (K layout)
+  const int vr = lane / LPR;  // key row within a V load instruction
+  const int vc = lane % LPR;  // 16-byte piece within the V row
+  uint4 qreg[G][NK];
+  {
+    const T* qb = (const T*)p.q + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+        qreg[h][j] = *(const uint4*)(qb + h * D + (c + 4 * j) * EPC);
+  }
+
+  const int64_t row_stride = (int64_t)p.num_kv_heads * D;  // elements per slot
+  const T* kbase = (const T*)p.k_pool + (int64_t)g * D;
+  const T* vbase = (const T*)p.v_pool + (int64_t)g * D;
+  const float sl2 = p.scale_log2;
+
+  float m_ref[G];   // wave-uniform reference maximum (log2 domain)
+  float l_acc[G];   // per-lane partial sum of weights (K layout)
+  float acc[G][EPC];  // per-lane partial output (V layout)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_ref[h] = -INFINITY;
+    l_acc[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
+  }
+
+  __syncthreads();  // s_slot ready
+
+  auto load_tile = [&](int ib, Tile<BF16, D, G>& tl) {
+    const int ik = ib + tq;
+    if (ik < n_tok) {
+      const T* kp = kbase + (int64_t)s_slot[ik] * row_stride;
+#pragma unroll
+      for (int j = 0; j < NK; ++j) tl.k[j] = *(const uint4*)(kp + (c + 4 * j) * EPC);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) tl.k[j] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int iv = ib + j * RPI + vr;
+      if (iv < n_tok)
+        tl.v[j] = *(const uint4*)(vbase + (int64_t)s_slot[iv] * row_stride + vc * EPC);
+      else
+        tl.v[j] = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  auto compute_tile = [&](int ib, const Tile<BF16, D, G>& tl) {
+    const bool valid = (ib + tq) < n_tok;
+    float sc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < NK; ++j) a = dot_piece<BF16>(qreg[h][j], tl.k[j], a);
+      a = quad_sum(a);
+      sc[h] = valid ? a * sl2 : -INFINITY;
+    }
+    bool over = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) over |= sc[h] > m_ref[h] + kRescaleSlack;
+    if (__ballot(over) != 0) {  // rare: raise the reference maximum
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mx = fmaxf(m_ref[h], wave_max(sc[h]));
+        const float alpha = fast_exp2(m_ref[h] - mx);
+        m_ref[h] = mx;
+        l_acc[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha;
+      }
+    }
+    float pw[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) pw[h] = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      pw[h] = fast_exp2(sc[h] - m_ref[h]);
+      l_acc[h] += pw[h];
+    }
+    // lanes of a quad hold identical weights; lane c publishes heads c, c+4
+    float* sp = reinterpret_cast<float*>(&s_p4[wave][tq][0]);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if ((h & 3) == c) sp[h] = pw[h];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int tv = j * RPI + vr;
+      float pv[GP];
+#pragma unroll
+      for (int h4 = 0; h4 < GP / 4; ++h4) {
+        const float4 x = s_p4[wave][tv][h4];
+        pv[4 * h4 + 0] = x.x; pv[4 * h4 + 1] = x.y; pv[4 * h4 + 2] = x.z; pv[4 * h4 + 3] = x.w;
+      }
+      float vf[EPC];
+      widen_piece<BF16>(tl.v[j], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // ---- main loop, two tiles in flight
+  constexpr int kStep = kDecodeWaves * kDecodeTokPerIter;
+  int ib = wave * kDecodeTokPerIter;
+  if (ib < n_tok) {
+    Tile<BF16, D, G> t0, t1;
+    load_tile(ib, t0);
+    while (true) {
+      int nb = ib + kStep;
+      if (nb < n_tok) load_tile(nb, t1);
+      compute_tile(ib, t0);
+      ib = nb;
+      if (ib >= n_tok) break;
+      nb = ib + kStep;
+      if (nb < n_tok) load_tile(nb, t0);
+      compute_tile(ib, t1);
+      ib = nb;
+      if (ib >= n_tok) break;
+    }
+  }
+
+  // ---- reduce within the wave
+  float l_w[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) l_w[h] = wave_sum(c == 0 ? l_acc[h] : 0.f);
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[h][e] += shfl_xor_f(acc[h][e], m);
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) s_acc[wave][h][vc * EPC + e] = acc[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_m[wave][h] = m_ref[h];
+      s_l[wave][h] = l_w[h];
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the waves and write the piece
+  const int64_t row0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = fast_exp2(s_m[w][h] - M);
+      lsum = fmaf(f, s_l[w][h], lsum);
+      o = fmaf(f, s_acc[w][h][d], o);
+    }
+    o = o / lsum;
+    if (n_splits == 1) {
+      if constexpr (BF16)
+        ((uint16_t*)p.out)[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
+      else
+        ((float*)p.out)[(row0 + h) * D + d] = o;
+    } else {
+      const int64_t r = (row0 + h) * S + s;
+      p.o_part[r * D + d] = o;
+      if (d == 0) p.lse[r] = M + __log2f(lsum);
+    }
+  }
+}
+
+// One wave per (request, query head): merge the request's pieces.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p) {
+  constexpr int EPL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
+  if (row >= rows) return;
+  const int b = (int)(row / p.num_q_heads);
+  const int L = p.seq_lens[b];
+  const int n = (L + p.split_tokens - 1) / p.split_tokens;
+  if (n == 1) return;  // written by the partial kernel
+  float res[EPL];
+  if (n == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) res[e] = 0.f;
+  } else {
+    const int S = p.max_splits;
+    const float* lse = p.lse + row * S;
+    float M = -INFINITY;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, lse[s]);
+    float wsum = 0.f;
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+    const float* op = p.o_part + row * S * D + lane * EPL;
+    for (int s = 0; s < n; ++s) {
+      const float w = fast_exp2(lse[s] - M);
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(w, op[(int64_t)s * D + e], o[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) res[e] = o[e] / wsum;
+  }
+  if constexpr (BF16) {
+    uint16_t* out = (uint16_t*)p.out + row * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(res[e]);
+  } else {
+    float* out = (float*)p.out + row * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = res[e];
+  }
+}
+
+template <bool BF16, int D, int G>
+hipError_t launch_partial_g(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.num_seqs * a.num_kv_heads * a.max_splits;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_partial_kernel<BF16, D, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_partial_d(const DecodeArgs& a, hipStream_t stream) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  switch (G) {
+    case 1: return launch_partial_g<BF16, D, 1>(a, stream);
+    case 2: return launch_partial_g<BF16, D, 2>(a, stream);
+    case 3: return launch_partial_g<BF16, D, 3>(a, stream);
+    case 4: return launch_partial_g<BF16, D, 4>(a, stream);
+    default: break;
+  }
+  if constexpr (BF16 || D == 64) {
+    switch (G) {
+      case 5: return launch_partial_g<BF16, D, 5>(a, stream);
+      case 6: return launch_partial_g<BF16, D, 6>(a, stream);
+      case 7: return launch_partial_g<BF16, D, 7>(a, stream);
+      case 8: return launch_partial_g<BF16, D, 8>(a, stream);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
+  if (a.bf16) {
+    if (a.head_dim == 128) return launch_partial_d<true, 128>(a, stream);
+    if (a.head_dim == 64) return launch_partial_d<true, 64>(a, stream);
+  } else {
+    if (a.head_dim == 128) return launch_partial_d<false, 128>(a, stream);
+    if (a.head_dim == 64) return launch_partial_d<false, 64>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (a.bf16) {
+    if (a.head_dim == 128) hipLaunchKernelGGL((decode_combine_kernel<true, 128>), grid, dim3(256), 0, stream, a);
+    else if (a.head_dim == 64) hipLaunchKernelGGL((decode_combine_kernel<true, 64>), grid, dim3(256), 0, stream, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (a.head_dim == 128) hipLaunchKernelGGL((decode_combine_kernel<false, 128>), grid, dim3(256), 0, stream, a);
+    else if (a.head_dim == 64) hipLaunchKernelGGL((decode_combine_kernel<false, 64>), grid, dim3(256), 0, stream, a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,89 @@
+// Store of new K/V rows into the paged pool, and the gather of requests'
+// pages back to contiguous rows.
+//
+// Store: the KV-cache write of each step ("mini-sglang from Scratch", section
+// "How this book works"); row i goes to flat slot slot_mapping[i], slots below
+// zero are padding.  Gather: the per-token copy out of the cache that the
+// legacy engine did every layer (nanoSGLang README, section Ablation); here it
+// is only a test of the page-table addressing and a bandwidth calibration.
+//
+// Both are plain byte copies: one 16-byte vector per lane, consecutive lanes
+// on consecutive 16-byte pieces of a row, so every wavefront load and store
+// covers whole 128-byte cache lines.
+#include "internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void kv_store_kernel(const uint4* __restrict__ k_new,
+                                                            const uint4* __restrict__ v_new,
+                                                            const int64_t* __restrict__ slots,
+                                                            uint4* __restrict__ k_pool,
+                                                            uint4* __restrict__ v_pool,
+                                                            int64_t total, int32_t row_chunks) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int64_t row = i / row_chunks;
+    const int64_t c = i - row * row_chunks;
+    const int64_t slot = slots[row];
+    if (slot < 0) continue;
+    const int64_t dst = slot * row_chunks + c;
+    k_pool[dst] = k_new[i];
+    v_pool[dst] = v_new[i];
+  }
+}
+
+// grid: (x = pieces of the longest request, y = request)
+__global__ __launch_bounds__(kThreads) void gather_kernel(const uint4* __restrict__ k_pool,
+                                                          const uint4* __restrict__ v_pool,
+                                                          const int32_t* __restrict__ page_table,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          const int64_t* __restrict__ out_offsets,
+                                                          uint4* __restrict__ k_out,
+                                                          uint4* __restrict__ v_out, int64_t pt_stride,
+                                                          int32_t log2_page, int32_t row_chunks) {
+  const int b = blockIdx.y;
+  const int64_t L = seq_lens[b];
+  const int64_t total = L * row_chunks;
+  const int32_t* pt = page_table + (int64_t)b * pt_stride;
+  const int32_t pmask = (1 << log2_page) - 1;
+  const int64_t base = out_offsets[b] * row_chunks;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int32_t t = (int32_t)(i / row_chunks);
+    const int64_t c = i - (int64_t)t * row_chunks;
+    const int64_t slot = ((int64_t)pt[t >> log2_page] << log2_page) | (t & pmask);
+    const int64_t src = slot * row_chunks + c;
+    k_out[base + i] = k_pool[src];
+    v_out[base + i] = v_pool[src];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream) {
+  const int64_t total = a.num_rows * a.row_chunks;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(kv_store_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     (const uint4*)a.k_new, (const uint4*)a.v_new, a.slot_mapping, (uint4*)a.k_pool,
+                     (uint4*)a.v_pool, total, a.row_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0 || a.max_seq_len == 0) return hipSuccess;
+  int64_t blocks = ((int64_t)a.max_seq_len * a.row_chunks + kThreads - 1) / kThreads;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks, (unsigned)a.num_seqs), dim3(kThreads), 0,
+                     stream, (const uint4*)a.k_pool, (const uint4*)a.v_pool, a.page_table, a.seq_lens,
+                     a.out_offsets, (uint4*)a.k_out, (uint4*)a.v_out, a.pt_stride, a.log2_page,
+                     a.row_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,168 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before any HIP call (so
+these run without a GPU; no call here reaches a kernel launch)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import paged_kv_attention_11_amd as pa
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "pagedattn.h"
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS = 0, 1, 2, 3, 4, 5
+
+
+def header_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pa.load()
+    names = header_functions()
+    assert "pa_decode" in names and "pa_kv_store" in names and "pa_extend" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pagedattn.h but not exported"
+    assert set(names) == set(pa.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_version_and_status_strings():
+    lib = pa.load()
+    assert b"gfx950" in lib.pa_version()
+    for s in range(7):
+        assert lib.pa_status_string(s) and lib.pa_status_string(s) != b"unknown status"
+    assert lib.pa_status_string(99) == b"unknown status"
+
+
+FAKE = 0x7F0000000000  # never dereferenced: validation returns first
+
+
+def pool(dtype=1, P=16, H=8, D=128, n=100, k=FAKE, v=FAKE + 0x10000000):
+    return pa.KVPool(k, v, n, P, H, D, dtype)
+
+
+def store(p, k=FAKE, v=FAKE, slots=FAKE, n=4):
+    return pa.load().pa_kv_store(ctypes.byref(p) if p is not None else None, k, v, slots, n, None)
+
+
+def decode(p, fn="pa_decode", q=FAKE, Hq=32, pt=FAKE, stride=64, sl=FAKE, B=4, Lmax=1000, split=0,
+           out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return getattr(pa.load(), fn)(ctypes.byref(p) if p is not None else None, q, Hq, pt, stride, sl, B,
+                                  Lmax, 0.1, split, out, ws, ws_bytes, None)
+
+
+def extend(p, q=FAKE, Hq=32, qi=FAKE, pt=FAKE, stride=64, sl=FAKE, B=2, qmax=128, Lmax=1000, out=FAKE):
+    return pa.load().pa_extend(ctypes.byref(p) if p is not None else None, q, Hq, qi, pt, stride, sl, B,
+                               qmax, Lmax, 0.1, out, None)
+
+
+def gather(p, pt=FAKE, stride=64, sl=FAKE, off=FAKE, B=2, Lmax=100, ko=FAKE, vo=FAKE):
+    return pa.load().pa_gather(ctypes.byref(p), pt, stride, sl, off, B, Lmax, ko, vo, None)
+
+
+@pytest.mark.parametrize("fn", ["store", "decode", "extend"])
+def test_pool_validation(fn):
+    call = {"store": store, "decode": decode, "extend": extend}[fn]
+    assert call(None) == NULL
+    assert call(pool(k=0)) == NULL
+    assert call(pool(v=0)) == NULL
+    assert call(pool(dtype=7)) == DTYPE
+    assert call(pool(D=96)) == UNSUP
+    assert call(pool(D=256)) == UNSUP
+    assert call(pool(P=3)) == UNSUP
+    assert call(pool(P=512)) == UNSUP
+    assert call(pool(n=0)) == SHAPE
+    assert call(pool(H=0)) == SHAPE
+    assert call(pool(k=FAKE + 8)) == SHAPE  # misaligned
+    assert call(pool(n=1 << 28, P=16)) == SHAPE  # more than 2^31 slots
+
+
+def test_store_validation():
+    p = pool()
+    assert store(p, n=-1) == SHAPE
+    assert store(p, n=0) == OK  # no-op, nothing launched
+    assert store(p, k=0) == NULL
+    assert store(p, slots=0) == NULL
+    assert store(p, v=FAKE + 4) == SHAPE
+
+
+def test_decode_validation():
+    p = pool()
+    for fn in ("pa_decode", "pa_decode_partial", "pa_decode_combine"):
+        assert decode(p, fn, Hq=30) == SHAPE  # not a multiple of H_kv
+        assert decode(p, fn, Hq=72) == UNSUP  # group 9
+        assert decode(p, fn, B=-1) == SHAPE
+        assert decode(p, fn, Lmax=-1) == SHAPE
+        assert decode(p, fn, stride=10) == SHAPE  # 10 * 16 < 1000
+        assert decode(p, fn, split=100) == SHAPE
+        assert decode(p, fn, split=2048) == SHAPE
+        assert decode(p, fn, q=0) == NULL
+        assert decode(p, fn, pt=0) == NULL
+        assert decode(p, fn, sl=0) == NULL
+        assert decode(p, fn, out=0) == NULL
+        assert decode(p, fn, ws=0) == WS
+        assert decode(p, fn, ws=FAKE + 16) == WS  # not 256-byte aligned
+        assert decode(p, fn, ws_bytes=1000) == WS
+        assert decode(p, fn, q=FAKE + 2) == SHAPE
+        assert decode(p, fn, B=0, q=0, pt=0, sl=0, out=0, ws=0) == OK  # empty batch: no-op
+    f32 = pool(dtype=0, D=128, H=8)
+    assert decode(f32, Hq=40) == UNSUP  # fp32: group 5 x 128 > 512
+
+
+def test_decode_workspace_size_matches_layout():
+    lib = pa.load()
+    # 256 requests, 32/8 heads, D=128, 8192 keys: automatic split 512 -> 16 pieces
+    assert lib.pa_decode_split_tokens(256, 8, 8192) == 512
+    S = 16
+    rows = 256 * 32 * S
+    expect = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 0) == expect
+    assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 100) == 0  # invalid split
+    assert lib.pa_decode_workspace_bytes(-1, 32, 8, 128, 8192, 0) == 0
+
+
+@pytest.mark.parametrize("B,H,L,expect", [
+    (4, 1, 64, 64),        # tiny decode
+    (32, 2, 640, 64),      # Qwen2.5-0.5B shape
+    (64, 8, 2048, 512),    # Qwen3-0.6B shape
+    (256, 8, 8192, 512),   # Qwen3-8B shape
+    (1, 1, 100000, 64),    # one long request: many short pieces fill the chip
+    (0, 8, 100, 64),
+])
+def test_automatic_split(B, H, L, expect):
+    s = pa.load().pa_decode_split_tokens(B, H, L)
+    assert s == expect and s % 64 == 0 and 64 <= s <= 1024
+
+
+def test_extend_validation():
+    p = pool()
+    assert extend(pool(dtype=0)) == DTYPE
+    assert extend(p, Hq=24) == UNSUP  # group 3
+    assert extend(p, Hq=30) == SHAPE
+    assert extend(p, qmax=2000) == SHAPE  # longer than max_seq_len
+    assert extend(p, stride=8) == SHAPE
+    assert extend(p, q=0) == NULL
+    assert extend(p, qi=0) == NULL
+    assert extend(p, out=0) == NULL
+    assert extend(p, out=FAKE + 4) == SHAPE
+    assert extend(p, B=0) == OK
+    assert extend(p, qmax=0) == OK
+
+
+def test_gather_validation():
+    p = pool()
+    assert gather(p, ko=0) == NULL
+    assert gather(p, off=0) == NULL
+    assert gather(p, B=70000) == UNSUP
+    assert gather(p, stride=2) == SHAPE
+    assert gather(p, B=0) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    k = torch.zeros(4, 16, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pa.kv_store(k, k, k[0], k[0], torch.zeros(1, dtype=torch.int64))

@@ -401,3 +401,48 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact); used by tests to read back
     GPU outputs."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# device copies (plumbing for the GPU tests and the benchmark)
+# --------------------------------------------------------------------------
+@dataclass
+class DeviceWorkload:
+    k_pool: "object"
+    v_pool: "object"
+    q: "object"
+    k_new: "object"
+    v_new: "object"
+    slot_mapping: "object"
+    page_table: "object"
+    seq_lens: "object"
+    q_indptr: "object"
+
+
+def to_device(wl: Workload, device="cuda") -> DeviceWorkload:
+    """torch copies of a workload's arrays (pools before the store)."""
+    import torch
+
+    def t(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+    def i(x, dt):
+        return torch.from_numpy(np.ascontiguousarray(x).astype(dt)).to(device)
+
+    return DeviceWorkload(
+        k_pool=t(wl.k_pool), v_pool=t(wl.v_pool), q=t(wl.q), k_new=t(wl.k_new), v_new=t(wl.v_new),
+        slot_mapping=i(wl.slot_mapping, np.int64), page_table=i(wl.page_table, np.int32),
+        seq_lens=i(wl.seq_lens, np.int32), q_indptr=i(wl.q_indptr, np.int32))
+
+
+def to_numpy_storage(t, dtype: str) -> np.ndarray:
+    """A device tensor back to the storage format used here (uint16 bits for
+    bf16)."""
+    import torch
+
+    x = t.detach().cpu()
+    if dtype == "bf16":
+        return x.view(torch.int16).numpy().view(np.uint16)
+    return x.numpy()

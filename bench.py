@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extend", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU leg")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only the plain-copy calibration (for hardware-counter scaling runs)")
     return ap.parse_args()
 
 
@@ -76,6 +78,44 @@ def read_traffic(launch_units):
         return float(kv["hbm_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
+
+
+COPY_PAGES = 16384  # per pool: 16384 pages x 16 tokens x 8 heads x 128 x bf16 = 512 MiB
+
+
+def copy_calibration(iters=10):
+    """A plain copy of known size with the library's gather kernel: K and V
+    pools of 512 MiB each, laid out as one request with an identity page
+    table, so a launch reads 1 GiB and writes 1 GiB in long sequential runs.
+    Returns (read+write GB/s, bytes read per launch, average launch ms)."""
+    import torch
+
+    import paged_kv_attention_11_amd as pa
+
+    P, H, D = 16, 8, 128
+    k = torch.randn(COPY_PAGES, P, H, D, device="cuda").to(torch.bfloat16)
+    v = torch.randn(COPY_PAGES, P, H, D, device="cuda").to(torch.bfloat16)
+    n = COPY_PAGES * P
+    pt = torch.arange(COPY_PAGES, dtype=torch.int32, device="cuda")[None, :].contiguous()
+    sl = torch.tensor([n], dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, n], dtype=torch.int64, device="cuda")
+    ko = torch.empty(n, H, D, dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    f = lambda: pa.gather(k, v, pt, sl, offs, n, ko, vo)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        f()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    nread = 2 * k.numel() * k.element_size()
+    del k, v, ko, vo
+    torch.cuda.empty_cache()
+    return 2 * nread / (ms * 1e-3) / 1e9, nread, ms
 
 
 def cpu_baseline(wl, target_s):
@@ -118,7 +158,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(attention shards over KV heads with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
@@ -133,6 +173,14 @@ def main():
     torch.cuda.set_device(0)
     pa.load()
     dev_name = torch.cuda.get_device_name(0)
+
+    if args.copy_only:
+        gbps, nread, ms = copy_calibration()
+        print(json.dumps({"copy_calibration": {"GBps_read_plus_write": round(gbps, 1),
+                                               "bytes_read_per_launch": nread,
+                                               "bytes_written_per_launch": nread,
+                                               "launch_ms": round(ms, 4)}}), flush=True)
+        return
 
     # ---------------- decode step: store + partial + combine
     t0 = time.perf_counter()
@@ -261,6 +309,11 @@ def main():
                          "algorithmic_flops_per_launch": flops},
         }
         log(f"extend: {ems * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+
+    # ---------------- plain-copy reference on the same device
+    cgb, _, _ = copy_calibration()
+    result["copy_reference_GBps"] = round(cgb, 1)
+    log(f"plain copy: {cgb:.0f} GB/s read+write")
 
     # ---------------- CPU oracle on a bounded sample (rank 0, N=1 only)
     if not args.no_cpu_baseline:

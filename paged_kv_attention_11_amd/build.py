@@ -18,6 +18,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libpagedattn.so"
+INCLUDE = PKG.parent / "include"
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -57,7 +58,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> Path:
         raise RuntimeError(f"no HIP sources under {CSRC}")
     objs = [BUILD / (s.stem + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
-    cmds = [[HIPCC, *COMMON, "-c", str(s), "-o", str(o)] for s, o in zip(srcs, objs)]
+    cmds = [[HIPCC, *COMMON, "-I", str(INCLUDE), "-c", str(s), "-o", str(o)] for s, o in zip(srcs, objs)]
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB.with_suffix(".so.tmp")

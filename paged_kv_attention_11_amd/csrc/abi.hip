@@ -4,7 +4,7 @@
 // synchronises, and keeps no state.
 #include <limits.h>
 
-#include "../../include/pagedattn.h"
+#include "pagedattn.h"
 #include "internal.h"
 
 namespace {
@@ -18,7 +18,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Work-groups the automatic split plan aims for: about eight per compute unit
 // on a 256-CU device, enough to fill the chip and even out the tail.
 constexpr int64_t kTargetUnits = 2048;
-constexpr int kAutoMaxSplit = 512;
+constexpr int kAutoMaxSplit = 1024;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

@@ -93,13 +93,34 @@ __device__ __forceinline__ void widen_piece(const uint4& v, float* f) {
   }
 }
 
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 1
+#endif
+constexpr int DEPTH = PA_DECODE_DEPTH;  // tile buffers per wave
+
+// Waves per SIMD the register budget is sized for: one tile buffer, the
+// group's accumulators and scores, and a fixed remainder (queries live in LDS).
 template <bool BF16, int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeArgs p) {
+struct DecodeOcc {
+  using C = DecodeCfg<BF16, D, G>;
+  static constexpr int kEstVgprs = G * C::EPC + (C::NK + C::NV) * 4 * DEPTH + 2 * G + 36;
+  static constexpr int kWaves = 512 / kEstVgprs < 1 ? 1 : (512 / kEstVgprs > 8 ? 8 : 512 / kEstVgprs);
+};
+#ifdef PA_DECODE_MIN_WAVES
+#define PA_DECODE_WAVES(B, D, G) PA_DECODE_MIN_WAVES
+#else
+#define PA_DECODE_WAVES(B, D, G) (DecodeOcc<B, D, G>::kWaves)
+#endif
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_partial_kernel(
+    const DecodeArgs p) {
   using C = DecodeCfg<BF16, D, G>;
   using T = std::conditional_t<BF16, uint16_t, float>;
   constexpr int EPC = C::EPC, NK = C::NK, NV = C::NV, RPI = C::RPI, LPR = C::LPR, GP = C::GP;
 
   __shared__ int32_t s_slot[kMaxSplitTokens];
+  __shared__ uint4 s_q[G][C::CPR];
   __shared__ float4 s_p4[kDecodeWaves][kDecodeTokPerIter][GP / 4];
   __shared__ float s_acc[kDecodeWaves][G][D];
   __shared__ float s_m[kDecodeWaves][G];
@@ -107,14 +128,21 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index, marked wave-uniform so loop control stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  int bid = blockIdx.x;
+  // Work-group id -> (piece s, request b, KV head g) with the piece index
+  // slowest.  Consecutive ids go to the 8 XCDs in turn, so the XCD of a unit
+  // is (b * H_kv + g) mod 8: every XCD gets a fair share of every piece index
+  // (piece 0 exists for every request, the last pieces only for long ones),
+  // and the requests that share prefix pages run close together in time on
+  // the same XCD, where their common pages can be served from its L2.
   const int S = p.max_splits;
-  const int s = bid % S;
-  bid /= S;
-  const int g = bid % p.num_kv_heads;
-  const int b = bid / p.num_kv_heads;
+  const int units = p.num_seqs * p.num_kv_heads;
+  const int s = blockIdx.x / units;
+  const int bg = blockIdx.x - s * units;
+  const int g = bg % p.num_kv_heads;
+  const int b = bg / p.num_kv_heads;
 
   const int L = p.seq_lens[b];
   const int t_begin = s * p.split_tokens;
@@ -133,19 +161,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     }
   }
 
-  // ---- the group's queries, quad layout: lane c holds pieces c, c+4, ...
+  // ---- the group's queries, staged in LDS (read back per tile as broadcasts)
   const int c = lane & 3;
   const int tq = lane >> 2;  // key within the iteration (K layout)
   const int vr = lane / LPR;  // key row within a V load instruction
   const int vc = lane % LPR;  // 16-byte piece within the V row
-  uint4 qreg[G][NK];
   {
-    const T* qb = (const T*)p.q + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int j = 0; j < NK; ++j)
-        qreg[h][j] = *(const uint4*)(qb + h * D + (c + 4 * j) * EPC);
+    const uint4* qb = (const uint4*)((const T*)p.q + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D);
+    for (int i = tid; i < G * C::CPR; i += kThreads) (&s_q[0][0])[i] = qb[i];
   }
 
   const int64_t row_stride = (int64_t)p.num_kv_heads * D;  // elements per slot
@@ -164,25 +187,21 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
   }
 
-  __syncthreads();  // s_slot ready
+  __syncthreads();  // s_slot and s_q ready
 
+  // Loads are issued unconditionally: a key index past the piece is clamped to
+  // the piece's last key (a real row, so no NaN can enter; its weight is 0).
+  // With no branch around the loads the compiler can keep DEPTH-1 tiles in
+  // flight (a skipped load would force it to wait for every load).
   auto load_tile = [&](int ib, Tile<BF16, D, G>& tl) {
-    const int ik = ib + tq;
-    if (ik < n_tok) {
-      const T* kp = kbase + (int64_t)s_slot[ik] * row_stride;
+    const int ik = min(ib + tq, n_tok - 1);
+    const T* kp = kbase + (int64_t)s_slot[ik] * row_stride;
 #pragma unroll
-      for (int j = 0; j < NK; ++j) tl.k[j] = *(const uint4*)(kp + (c + 4 * j) * EPC);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NK; ++j) tl.k[j] = make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < NK; ++j) tl.k[j] = *(const uint4*)(kp + (c + 4 * j) * EPC);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int iv = ib + j * RPI + vr;
-      if (iv < n_tok)
-        tl.v[j] = *(const uint4*)(vbase + (int64_t)s_slot[iv] * row_stride + vc * EPC);
-      else
-        tl.v[j] = make_uint4(0, 0, 0, 0);
+      const int iv = min(ib + j * RPI + vr, n_tok - 1);
+      tl.v[j] = *(const uint4*)(vbase + (int64_t)s_slot[iv] * row_stride + vc * EPC);
     }
   };
 
@@ -190,11 +209,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     const bool valid = (ib + tq) < n_tok;
     float sc[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float a = 0.f;
+    for (int h = 0; h < G; ++h) sc[h] = 0.f;
 #pragma unroll
-      for (int j = 0; j < NK; ++j) a = dot_piece<BF16>(qreg[h][j], tl.k[j], a);
-      a = quad_sum(a);
+    for (int j = 0; j < NK; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = dot_piece<BF16>(s_q[h][c + 4 * j], tl.k[j], sc[h]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = quad_sum(sc[h]);
       sc[h] = valid ? a * sl2 : -INFINITY;
     }
     bool over = false;
@@ -248,23 +270,24 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeAr
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // ---- main loop, two tiles in flight
+  // ---- main loop: DEPTH tile buffers, DEPTH-1 tiles in flight while one is
+  // computed (buffer indices are compile-time after unrolling)
   constexpr int kStep = kDecodeWaves * kDecodeTokPerIter;
-  int ib = wave * kDecodeTokPerIter;
-  if (ib < n_tok) {
-    Tile<BF16, D, G> t0, t1;
-    load_tile(ib, t0);
-    while (true) {
-      int nb = ib + kStep;
-      if (nb < n_tok) load_tile(nb, t1);
-      compute_tile(ib, t0);
-      ib = nb;
-      if (ib >= n_tok) break;
-      nb = ib + kStep;
-      if (nb < n_tok) load_tile(nb, t0);
-      compute_tile(ib, t1);
-      ib = nb;
-      if (ib >= n_tok) break;
+  {
+    const int ib0 = wave * kDecodeTokPerIter;
+    if (ib0 < n_tok) {  // uniform over the wave
+      Tile<BF16, D, G> buf[DEPTH];
+#pragma unroll
+      for (int k = 0; k < DEPTH - 1; ++k) load_tile(ib0 + k * kStep, buf[k]);
+      for (int base = ib0; base < n_tok; base += DEPTH * kStep) {
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+          const int cur = base + k * kStep;
+          if (cur >= n_tok) break;
+          load_tile(cur + (DEPTH - 1) * kStep, buf[(k + DEPTH - 1) % DEPTH]);
+          compute_tile(cur, buf[k]);
+        }
+      }
     }
   }
 

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   const int col = lane & 31;  // query row within the wave
   const int half = lane >> 5;
 
-  // ---- work-group coordinates; heavier (later) token blocks first
+  // ---- work-group coordinates: the token blocks of one (request, KV head)
+  // are consecutive ids, heaviest (latest) first
   const int qblocks = (p.max_q_len + TOK - 1) / TOK;
   int bid = blockIdx.x;
   const int qb = qblocks - 1 - (bid % qblocks);

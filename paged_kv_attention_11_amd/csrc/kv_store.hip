@@ -36,7 +36,9 @@ __global__ __launch_bounds__(kThreads) void kv_store_kernel(const uint4* __restr
   }
 }
 
-// grid: (x = pieces of the longest request, y = request)
+// grid: (x = token blocks of the longest request, y = request).  A thread
+// owns one 16-byte piece of a row; `tpi` whole rows are copied per block
+// iteration (one row-piece per thread, so no division inside the loop).
 __global__ __launch_bounds__(kThreads) void gather_kernel(const uint4* __restrict__ k_pool,
                                                           const uint4* __restrict__ v_pool,
                                                           const int32_t* __restrict__ page_table,
@@ -46,19 +48,26 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint4* __restric
                                                           uint4* __restrict__ v_out, int64_t pt_stride,
                                                           int32_t log2_page, int32_t row_chunks) {
   const int b = blockIdx.y;
-  const int64_t L = seq_lens[b];
-  const int64_t total = L * row_chunks;
+  const int L = seq_lens[b];
   const int32_t* pt = page_table + (int64_t)b * pt_stride;
   const int32_t pmask = (1 << log2_page) - 1;
-  const int64_t base = out_offsets[b] * row_chunks;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
-    const int32_t t = (int32_t)(i / row_chunks);
-    const int64_t c = i - (int64_t)t * row_chunks;
+  const int64_t base = out_offsets[b];
+  const int rc = row_chunks;
+  const bool small = rc <= kThreads;
+  const int tpi = small ? kThreads / rc : 1;           // rows per block iteration
+  const int t_off = small ? (int)threadIdx.x / rc : 0;  // this thread's row in the iteration
+  const int c0 = small ? (int)threadIdx.x - t_off * rc : (int)threadIdx.x;
+  const int cstep = small ? rc : kThreads;
+  if (t_off >= tpi) return;
+#pragma unroll 4
+  for (int t = blockIdx.x * tpi + t_off; t < L; t += gridDim.x * tpi) {
     const int64_t slot = ((int64_t)pt[t >> log2_page] << log2_page) | (t & pmask);
-    const int64_t src = slot * row_chunks + c;
-    k_out[base + i] = k_pool[src];
-    v_out[base + i] = v_pool[src];
+    const int64_t src = slot * rc;
+    const int64_t dst = (base + t) * rc;
+    for (int c = c0; c < rc; c += cstep) {
+      k_out[dst + c] = k_pool[src + c];
+      v_out[dst + c] = v_pool[src + c];
+    }
   }
 }
 
@@ -77,7 +86,8 @@ hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream) {
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.max_seq_len == 0) return hipSuccess;
-  int64_t blocks = ((int64_t)a.max_seq_len * a.row_chunks + kThreads - 1) / kThreads;
+  const int tpi = a.row_chunks <= kThreads ? kThreads / a.row_chunks : 1;
+  int64_t blocks = ((int64_t)a.max_seq_len + tpi - 1) / tpi;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks, (unsigned)a.num_seqs), dim3(kThreads), 0,
                      stream, (const uint4*)a.k_pool, (const uint4*)a.v_pool, a.page_table, a.seq_lens,

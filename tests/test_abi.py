@@ -113,9 +113,9 @@ def test_decode_validation():
 
 def test_decode_workspace_size_matches_layout():
     lib = pa.load()
-    # 256 requests, 32/8 heads, D=128, 8192 keys: automatic split 512 -> 16 pieces
-    assert lib.pa_decode_split_tokens(256, 8, 8192) == 512
-    S = 16
+    # 256 requests, 32/8 heads, D=128, 8192 keys: automatic split 1024 -> 8 pieces
+    assert lib.pa_decode_split_tokens(256, 8, 8192) == 1024
+    S = 8
     rows = 256 * 32 * S
     expect = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 0) == expect
@@ -127,7 +127,7 @@ def test_decode_workspace_size_matches_layout():
     (4, 1, 64, 64),        # tiny decode
     (32, 2, 640, 64),      # Qwen2.5-0.5B shape
     (64, 8, 2048, 512),    # Qwen3-0.6B shape
-    (256, 8, 8192, 512),   # Qwen3-8B shape
+    (256, 8, 8192, 1024),  # Qwen3-8B shape
     (1, 1, 100000, 64),    # one long request: many short pieces fill the chip
     (0, 8, 100, 64),
 ])

@@ -83,6 +83,16 @@ struct Staged {
   uint2 v[ExtCfg<D>::V_PASSES][8];
 };
 
+// Byte permute (v_perm_b32): result byte i = byte sel[i] of the 8-byte value
+// {hi, lo} (lo = bytes 0..3).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+constexpr uint32_t kLoHalves = 0x05040100u;  // {lo.lo16, hi.lo16}
+constexpr uint32_t kHiHalves = 0x07060302u;  // {lo.hi16, hi.hi16}
+
+constexpr float kExtRescaleSlack = 8.0f;  // log2 units, as in decode
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   using C = ExtCfg<D>;
@@ -91,10 +101,11 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
 
   __shared__ uint4 s_k[2][kKT * PPR];
   __shared__ uint4 s_v[2][D * 8];
+  __shared__ int32_t s_slot[3][kKT];  // flat slots of the keys of tiles t, t+1, t+2
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;  // query row within the wave
   const int half = lane >> 5;
 
@@ -140,21 +151,21 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)g * D;
 
-  // Global loads of one key tile into registers.
+  // Slot of key (t*64 + tid) for the first 64 threads; keys past the block's
+  // range are clamped to its last key (a real row; masked out later), so no
+  // page-table entry past the request's pages is read.
+  auto slot_of = [&](int t) -> int32_t {
+    const int kk = min(t * kKT + tid, kv_len - 1);
+    return (pt[kk >> sh] << sh) | (kk & pmask);
+  };
+
+  // Global loads of tile t into registers; slots come from LDS.
   auto load_tile = [&](int t, Staged<D>& st) {
-    const int kt0 = t * kKT;
+    const int32_t* sl = s_slot[t % 3];
 #pragma unroll
     for (int j = 0; j < C::K_LOADS; ++j) {
       const int idx = j * kThreads + tid;
-      const int key = idx / PPR;
-      const int pc = idx % PPR;
-      const int kk = kt0 + key;
-      if (kk < kv_len) {
-        const int64_t slot = ((int64_t)pt[kk >> sh] << sh) | (kk & pmask);
-        st.k[j] = *(const uint4*)(kbase + slot * row_stride + pc * 8);
-      } else {
-        st.k[j] = make_uint4(0, 0, 0, 0);
-      }
+      st.k[j] = *(const uint4*)(kbase + (int64_t)sl[idx / PPR] * row_stride + (idx % PPR) * 8);
     }
     // V: an item is 4 head-dim elements of the 8 keys forming one transposed
     // piece: keys 16*(kp/2) + 4*(kp%2) + {0,1,2,3,8,9,10,11}.
@@ -164,17 +175,10 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
       if (item >= C::V_ITEMS) break;
       const int dg = item % C::VDG;
       const int kp = item / C::VDG;
-      const int kbase16 = 16 * (kp >> 1) + 4 * (kp & 1);
+      const int k16 = 16 * (kp >> 1) + 4 * (kp & 1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = kt0 + kbase16 + (e & 3) + ((e >> 2) << 3);
-        if (kk < kv_len) {
-          const int64_t slot = ((int64_t)pt[kk >> sh] << sh) | (kk & pmask);
-          st.v[ps][e] = *(const uint2*)(vbase + slot * row_stride + dg * 4);
-        } else {
-          st.v[ps][e] = make_uint2(0, 0);
-        }
-      }
+      for (int e = 0; e < 8; ++e)
+        st.v[ps][e] = *(const uint2*)(vbase + (int64_t)sl[k16 + (e & 3) + ((e >> 2) << 3)] * row_stride + dg * 4);
     }
   };
 
@@ -193,14 +197,14 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
       const uint2* x = st.v[ps];
       // transpose 8 keys x 4 dims -> 4 rows (dims) of 8 keys
       uint4 r[4];
-      r[0] = make_uint4((x[0].x & 0xffffu) | (x[1].x << 16), (x[2].x & 0xffffu) | (x[3].x << 16),
-                        (x[4].x & 0xffffu) | (x[5].x << 16), (x[6].x & 0xffffu) | (x[7].x << 16));
-      r[1] = make_uint4((x[0].x >> 16) | (x[1].x & 0xffff0000u), (x[2].x >> 16) | (x[3].x & 0xffff0000u),
-                        (x[4].x >> 16) | (x[5].x & 0xffff0000u), (x[6].x >> 16) | (x[7].x & 0xffff0000u));
-      r[2] = make_uint4((x[0].y & 0xffffu) | (x[1].y << 16), (x[2].y & 0xffffu) | (x[3].y << 16),
-                        (x[4].y & 0xffffu) | (x[5].y << 16), (x[6].y & 0xffffu) | (x[7].y << 16));
-      r[3] = make_uint4((x[0].y >> 16) | (x[1].y & 0xffff0000u), (x[2].y >> 16) | (x[3].y & 0xffff0000u),
-                        (x[4].y >> 16) | (x[5].y & 0xffff0000u), (x[6].y >> 16) | (x[7].y & 0xffff0000u));
+      r[0] = make_uint4(perm(x[1].x, x[0].x, kLoHalves), perm(x[3].x, x[2].x, kLoHalves),
+                        perm(x[5].x, x[4].x, kLoHalves), perm(x[7].x, x[6].x, kLoHalves));
+      r[1] = make_uint4(perm(x[1].x, x[0].x, kHiHalves), perm(x[3].x, x[2].x, kHiHalves),
+                        perm(x[5].x, x[4].x, kHiHalves), perm(x[7].x, x[6].x, kHiHalves));
+      r[2] = make_uint4(perm(x[1].y, x[0].y, kLoHalves), perm(x[3].y, x[2].y, kLoHalves),
+                        perm(x[5].y, x[4].y, kLoHalves), perm(x[7].y, x[6].y, kLoHalves));
+      r[3] = make_uint4(perm(x[1].y, x[0].y, kHiHalves), perm(x[3].y, x[2].y, kHiHalves),
+                        perm(x[5].y, x[4].y, kHiHalves), perm(x[7].y, x[6].y, kHiHalves));
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_v[buf][v_lds_off(dg * 4 + i, kp)] = r[i];
     }
@@ -211,10 +215,17 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  float m_run = -INFINITY;  // running maximum of this row (log2 domain)
+  float m_ref = -INFINITY;  // reference maximum of this row's raw scores
   float l_run = 0.f;        // this lane's half of the running sum
   const float sl2 = p.scale_log2;
+  const float slack = kExtRescaleSlack / sl2;  // the same slack in raw-score units
 
+  // ---- prologue: slots of tiles 0 and 1, then tile 0 into LDS
+  if (tid < kKT) {
+    s_slot[0][tid] = slot_of(0);
+    if (ntiles > 1) s_slot[1][tid] = slot_of(1);
+  }
+  __syncthreads();
   {
     Staged<D> st;
     load_tile(0, st);
@@ -227,6 +238,9 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
     Staged<D> st;
     const bool more = (t + 1) < ntiles;
     if (more) load_tile(t + 1, st);
+    int32_t next_slot = 0;
+    const bool fill = (t + 2) < ntiles && tid < kKT;
+    if (fill) next_slot = slot_of(t + 2);
 
     // ---- S^T = K Q^T for two 32-key halves of the tile
     f32x16_t s[2];
@@ -242,47 +256,54 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
       }
     }
 
-    // ---- mask, online softmax (lane owns one query row, half the keys)
+    // ---- causal mask, only on tiles that cross the diagonal (block-uniform)
     const int kt0 = t * kKT;
-    const bool diag = kt0 + kKT - 1 > prefix + i0;  // tile may cross the diagonal
+    if (kt0 + kKT - 1 > prefix + i0) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > vis_lim) s[kt][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (lane owns one query row, half of the tile's keys);
+    // the reference maximum moves only when exceeded by the slack
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[kt][r] * sl2;
-        if (diag) {
-          const int key = kt0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > vis_lim) v = -INFINITY;
-        }
-        s[kt][r] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: key 0 of tile 0 is visible to every row
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f;
+    if (__ballot(mx > m_ref + slack) != 0) {
+      const float m_new = fmaxf(m_ref, mx);  // finite: key 0 of tile 0 is visible to every row
+      const float alpha = fast_exp2((m_ref - m_new) * sl2);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+    const float mb = -m_ref * sl2;
     uint4 pb[4];  // B operands of the four 16-key steps
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(s[kt][r] - m_new);
-        lsum += e[r];
+        e[r] = fast_exp2(fmaf(s[kt][r], sl2, mb));
+        l_run += e[r];
       }
       pb[2 * kt + 0] = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
       pb[2 * kt + 1] =
           make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
     }
-    l_run = l_run * alpha + lsum;
 
-    // ---- O^T = alpha * O^T + V^T P^T
+    // ---- O^T += V^T P^T
 #pragma unroll
     for (int i = 0; i < DT; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
       const int d = i * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -292,6 +313,7 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
     }
 
     if (more) store_tile(buf ^ 1, st);
+    if (fill) s_slot[(t + 2) % 3][tid] = next_slot;
     __syncthreads();
   }
 

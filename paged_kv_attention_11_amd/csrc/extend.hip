@@ -38,6 +38,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRows = 128;  // query rows per work-group
@@ -57,39 +58,57 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 template <int D>
 struct ExtCfg {
-  static constexpr int PPR = D / 8;            // 16-byte pieces per K row
-  static constexpr int KSTEPS = D / 16;        // MFMA k-steps over head_dim
-  static constexpr int DT = D / 32;            // 32-row tiles of O^T
-  static constexpr int K_LOADS = kKT * PPR / kThreads;        // K pieces per thread per tile
-  static constexpr int VDG = D / 4;            // V load: groups of 4 head-dim elements
-  static constexpr int V_ITEMS = VDG * 8;      // (dim group, 8-key piece) items per tile
-  static constexpr int V_PASSES = (V_ITEMS + kThreads - 1) / kThreads;
-  static_assert(K_LOADS >= 1, "tile too small");
-  static_assert(V_ITEMS % kThreads == 0 || V_ITEMS < kThreads, "bad V split");
+  static constexpr int PPR = D / 8;          // 16-byte pieces per K/V row
+  static constexpr int KSTEPS = D / 16;      // MFMA k-steps over head_dim
+  static constexpr int DT = D / 32;          // 32-row tiles of O^T
+  static constexpr int RPB = 64 / PPR;       // rows per 1 KB LDS block (one DMA instruction)
+  static constexpr int NDMA = kKT * PPR / kThreads;  // DMA instructions per thread per tile, per tensor
+  static_assert(NDMA >= 1 && kKT * PPR % kThreads == 0, "bad tile");
 };
 
-// Swizzled position (in 16-byte units) of piece `pc` of K row `key`.
-template <int D>
-__device__ __forceinline__ int k_lds_off(int key, int pc) {
-  constexpr int PPR = D / 8;
-  return key * PPR + (pc ^ (key & (PPR - 1)));
-}
-// Swizzled position of key piece `kp` (0..7) of V^T row `d`.
-__device__ __forceinline__ int v_lds_off(int d, int kp) { return d * 8 + (kp ^ (d & 7)); }
+constexpr int kStages = 3;      // LDS ring depth: tiles t (computed), t+1, t+2 (in flight)
+constexpr int kPageCap = 1024;  // page ids staged in LDS at a time
 
+// K rows: 16-byte piece p of key k is stored at piece p ^ (k mod PPR), so the
+// 32 keys read by one MFMA operand fetch hit distinct banks.
 template <int D>
-struct Staged {
-  uint4 k[ExtCfg<D>::K_LOADS];
-  uint2 v[ExtCfg<D>::V_PASSES][8];
-};
+__device__ __forceinline__ int k_swz(int key) { return key & (ExtCfg<D>::PPR - 1); }
+// V rows: piece p of key k at p ^ 2(k mod 4), so the 4 keys x 32 bytes of one
+// transposing read group fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int v_swz(int key) { return (2 * (key & 3)) & (ExtCfg<D>::PPR - 1); }
 
-// Byte permute (v_perm_b32): result byte i = byte sel[i] of the 8-byte value
-// {hi, lo} (lo = bytes 0..3).
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
 }
-constexpr uint32_t kLoHalves = 0x05040100u;  // {lo.lo16, hi.lo16}
-constexpr uint32_t kHiHalves = 0x07060302u;  // {lo.hi16, hi.hi16}
+
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's 16 bytes land at LDS address `lds` + 16 i.  Issued as inline asm so
+// the compiler's wait-count pass does not serialise it against unrelated LDS
+// reads; completion is awaited explicitly with vm_wait below.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j supplies the address of 4 consecutive 16-bit values; lane i receives
+// value (i mod 4) of the chunks of lanes i/4, i/4+4, i/4+8, i/4+12.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* ptr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)ptr);
+  return __builtin_bit_cast(uint2, v);
+#else
+  (void)ptr;
+  return make_uint2(0, 0);
+#endif
+}
 
 constexpr float kExtRescaleSlack = 8.0f;  // log2 units, as in decode
 
@@ -97,11 +116,11 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   using C = ExtCfg<D>;
   constexpr int TOK = kRows / G;  // tokens per work-group
-  constexpr int KSTEPS = C::KSTEPS, DT = C::DT, PPR = C::PPR;
+  constexpr int KSTEPS = C::KSTEPS, DT = C::DT, PPR = C::PPR, NDMA = C::NDMA;
 
-  __shared__ uint4 s_k[2][kKT * PPR];
-  __shared__ uint4 s_v[2][D * 8];
-  __shared__ int32_t s_slot[3][kKT];  // flat slots of the keys of tiles t, t+1, t+2
+  __shared__ uint4 s_k[kStages][kKT * PPR];
+  __shared__ uint4 s_v[kStages][kKT * PPR];
+  __shared__ int32_t s_pages[kPageCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,6 +161,14 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
       qreg[ks] = qvalid ? *(const uint4*)(qp + ks * 16 + half * 8) : make_uint4(0, 0, 0, 0);
+    // Retire the query loads here, once: after this the registers' last
+    // writer is not a memory load, so the loop below carries no wait for them.
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4_t v = __builtin_bit_cast(u32x4_t, qreg[ks]);
+      asm volatile("" : "+v"(v));
+      qreg[ks] = __builtin_bit_cast(uint4, v);
+    }
   }
 
   const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride;
@@ -150,63 +177,31 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   const int64_t row_stride = (int64_t)p.num_kv_heads * D;  // elements per slot
   const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)g * D;
+  const int chunk_keys = kPageCap << sh;  // keys covered by one staging of page ids
+  const int npages = ((kv_len - 1) >> sh) + 1;
 
-  // Slot of key (t*64 + tid) for the first 64 threads; keys past the block's
-  // range are clamped to its last key (a real row; masked out later), so no
-  // page-table entry past the request's pages is read.
-  auto slot_of = [&](int t) -> int32_t {
-    const int kk = min(t * kKT + tid, kv_len - 1);
-    return (pt[kk >> sh] << sh) | (kk & pmask);
+  // Page ids of chunk c (pages c*kPageCap ...) into LDS; entries past the
+  // block's last page are not read.
+  auto stage_pages = [&](int c) {
+    const int base = c * kPageCap;
+    for (int i = tid; i < kPageCap; i += kThreads)
+      if (base + i < npages) s_pages[i] = pt[base + i];
   };
 
-  // Global loads of tile t into registers; slots come from LDS.
-  auto load_tile = [&](int t, Staged<D>& st) {
-    const int32_t* sl = s_slot[t % 3];
+  // DMA of tile t into ring slot sb: each wave fills NDMA 1 KB blocks of K and
+  // of V.  Keys past the block's range are clamped to its last key (a real
+  // row; masked out of the softmax).
+  auto issue_tile = [&](int t, int sb, int chunk) {
+    const int pc = lane % PPR;
 #pragma unroll
-    for (int j = 0; j < C::K_LOADS; ++j) {
-      const int idx = j * kThreads + tid;
-      st.k[j] = *(const uint4*)(kbase + (int64_t)sl[idx / PPR] * row_stride + (idx % PPR) * 8);
-    }
-    // V: an item is 4 head-dim elements of the 8 keys forming one transposed
-    // piece: keys 16*(kp/2) + 4*(kp%2) + {0,1,2,3,8,9,10,11}.
-#pragma unroll
-    for (int ps = 0; ps < C::V_PASSES; ++ps) {
-      const int item = ps * kThreads + tid;
-      if (item >= C::V_ITEMS) break;
-      const int dg = item % C::VDG;
-      const int kp = item / C::VDG;
-      const int k16 = 16 * (kp >> 1) + 4 * (kp & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        st.v[ps][e] = *(const uint2*)(vbase + (int64_t)sl[k16 + (e & 3) + ((e >> 2) << 3)] * row_stride + dg * 4);
-    }
-  };
-
-  auto store_tile = [&](int buf, const Staged<D>& st) {
-#pragma unroll
-    for (int j = 0; j < C::K_LOADS; ++j) {
-      const int idx = j * kThreads + tid;
-      s_k[buf][k_lds_off<D>(idx / PPR, idx % PPR)] = st.k[j];
-    }
-#pragma unroll
-    for (int ps = 0; ps < C::V_PASSES; ++ps) {
-      const int item = ps * kThreads + tid;
-      if (item >= C::V_ITEMS) break;
-      const int dg = item % C::VDG;
-      const int kp = item / C::VDG;
-      const uint2* x = st.v[ps];
-      // transpose 8 keys x 4 dims -> 4 rows (dims) of 8 keys
-      uint4 r[4];
-      r[0] = make_uint4(perm(x[1].x, x[0].x, kLoHalves), perm(x[3].x, x[2].x, kLoHalves),
-                        perm(x[5].x, x[4].x, kLoHalves), perm(x[7].x, x[6].x, kLoHalves));
-      r[1] = make_uint4(perm(x[1].x, x[0].x, kHiHalves), perm(x[3].x, x[2].x, kHiHalves),
-                        perm(x[5].x, x[4].x, kHiHalves), perm(x[7].x, x[6].x, kHiHalves));
-      r[2] = make_uint4(perm(x[1].y, x[0].y, kLoHalves), perm(x[3].y, x[2].y, kLoHalves),
-                        perm(x[5].y, x[4].y, kLoHalves), perm(x[7].y, x[6].y, kLoHalves));
-      r[3] = make_uint4(perm(x[1].y, x[0].y, kHiHalves), perm(x[3].y, x[2].y, kHiHalves),
-                        perm(x[5].y, x[4].y, kHiHalves), perm(x[7].y, x[6].y, kHiHalves));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_v[buf][v_lds_off(dg * 4 + i, kp)] = r[i];
+    for (int m = 0; m < NDMA; ++m) {
+      const int blk = wave * NDMA + m;
+      const int key = blk * C::RPB + lane / PPR;
+      const int kk = min(t * kKT + key, kv_len - 1);
+      const int32_t page = s_pages[(kk >> sh) - chunk * kPageCap];
+      const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride;
+      dma16(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(key)) * 8);
+      dma16(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(key)) * 8);
     }
   };
 
@@ -220,27 +215,29 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   const float sl2 = p.scale_log2;
   const float slack = kExtRescaleSlack / sl2;  // the same slack in raw-score units
 
-  // ---- prologue: slots of tiles 0 and 1, then tile 0 into LDS
-  if (tid < kKT) {
-    s_slot[0][tid] = slot_of(0);
-    if (ntiles > 1) s_slot[1][tid] = slot_of(1);
-  }
+  // ---- prologue: page ids, then tiles 0 and 1 in flight
+  int chunk = 0;
+  stage_pages(0);
   __syncthreads();
-  {
-    Staged<D> st;
-    load_tile(0, st);
-    store_tile(0, st);
-  }
+  issue_tile(0, 0, 0);
+  if (ntiles > 1) issue_tile(1, 1, 0);  // chunk_keys >= 1024, so tiles 0 and 1 share chunk 0
+  if (ntiles > 1) vm_wait<2 * NDMA>(); else vm_wait<0>();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    Staged<D> st;
-    const bool more = (t + 1) < ntiles;
-    if (more) load_tile(t + 1, st);
-    int32_t next_slot = 0;
-    const bool fill = (t + 2) < ntiles && tid < kKT;
-    if (fill) next_slot = slot_of(t + 2);
+    const int buf = t % kStages;
+    const bool ahead = (t + 2) < ntiles;
+    if (ahead) {
+      const int c2 = ((t + 2) * kKT) / chunk_keys;
+      if (c2 != chunk) {  // block-uniform and rare: restage page ids
+        vm_wait<0>();
+        __syncthreads();
+        stage_pages(c2);
+        chunk = c2;
+        __syncthreads();
+      }
+      issue_tile(t + 2, (t + 2) % kStages, chunk);
+    }
 
     // ---- S^T = K Q^T for two 32-key halves of the tile
     f32x16_t s[2];
@@ -251,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
       const int key = kt * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const uint4 a = s_k[buf][k_lds_off<D>(key, 2 * ks + half)];
+        const uint4 a = s_k[buf][key * PPR + ((2 * ks + half) ^ k_swz<D>(key))];
         s[kt] = mfma32(a, qreg[ks], s[kt]);
       }
     }
@@ -301,19 +298,31 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
           make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; the A operand is read transposed out of row-major V:
+    // lane (group gq of 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims
+    // d0 + 4(j%4) .. +3 and receives V[4 keys][d0 + j]
+    {
+      const int grp = lane >> 4, j = lane & 15;
+      const char* vb = (const char*)&s_v[buf][0];
 #pragma unroll
-    for (int i = 0; i < DT; ++i) {
-      const int d = i * 32 + col;
+      for (int i = 0; i < DT; ++i) {
+        const int d = i * 32 + 16 * (grp & 1) + 4 * (j & 3);
+        const int lp = d >> 3;              // logical 16-byte piece
+        const int within = (d & 4) ? 8 : 0;  // byte offset inside the piece
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 a = s_v[buf][v_lds_off(d, 2 * ks + half)];
-        o[i] = mfma32(a, pb[ks], o[i]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const int k0 = 16 * ks + 4 * half + (j >> 2);
+          const int k1 = k0 + 8;
+          const uint2 x0 = lds_read_tr16(vb + (k0 * PPR + (lp ^ v_swz<D>(k0))) * 16 + within);
+          const uint2 x1 = lds_read_tr16(vb + (k1 * PPR + (lp ^ v_swz<D>(k1))) * 16 + within);
+          o[i] = mfma32(make_uint4(x0.x, x0.y, x1.x, x1.y), pb[ks], o[i]);
+        }
       }
     }
 
-    if (more) store_tile(buf ^ 1, st);
-    if (fill) s_slot[(t + 2) % 3][tid] = next_slot;
+    // tile t+1 must have landed (tile t+2 may still be in flight) before the
+    // next iteration reads it; the barrier also retires this tile's reads
+    if (ahead) vm_wait<2 * NDMA>(); else vm_wait<0>();
     __syncthreads();
   }
 

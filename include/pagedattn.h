@@ -21,6 +21,15 @@
  *                  sections Reference Attention Backends and Speculative
  *                  Decoding; nanollmserve README, section v0.7 Chunked
  *                  Prefill);
+ *   pa_decode_cascade
+ *                  the result of pa_decode, computed for requests whose
+ *                  leading pages are shared through a prefix cache (the radix
+ *                  tree of nanoSGLang README, section Architecture; prefix
+ *                  match in the mini-sglang README, TODO list; the radix
+ *                  cache with matching and reference counting of "mini-sglang
+ *                  from Scratch", section "What you will be able to do"):
+ *                  each shared page is read once per group of requests
+ *                  instead of once per request;
  *   pa_gather      copy requests' pages out to contiguous K/V (test and
  *                  calibration helper: the legacy per-token copy that paged
  *                  attention removes, nanoSGLang README, section Ablation).
@@ -178,6 +187,66 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                     const int32_t* q_indptr, const int32_t* page_table, int32_t pt_stride,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t max_q_len,
                     int32_t max_seq_len, float scale, void* out, void* stream);
+
+/*
+ * Cascade (prefix-aware) decode.  The requests are cut into consecutive
+ * groups: group j is requests group_starts[j] .. group_starts[j+1] - 1
+ * (group_starts int32 [num_groups + 1], device, non-decreasing, from 0 to
+ * num_seqs, so every request is in exactly one group; a request that shares
+ * nothing is a group of its own with shared_len 0).  The first
+ * shared_lens[b] keys of request b (int32 [num_seqs], device) are keys
+ * 0 .. shared_lens[b] - 1 of its group's prefix pages, prefix_page_table row
+ * j (int32 [num_groups, prefix_pt_stride], device); they must be the same
+ * pages as the first entries of the request's own page_table row.
+ *
+ * The result is that of pa_decode with the same q, page_table and seq_lens,
+ * up to floating-point rounding.  Three kernels are enqueued:
+ *   1. per (group, KV head, key piece of prefix_piece_keys keys): every
+ *      member's query heads of the KV head against the group's prefix keys,
+ *      on the matrix cores (each tile of shared K/V is read once per group);
+ *   2. per (request, KV head, piece of split_tokens keys): the request's own
+ *      keys shared_lens[b] .. seq_lens[b] - 1, as in pa_decode_partial;
+ *   3. per (request, query head): merge of both sets of pieces by
+ *      log-sum-exp weights.
+ * Scores and the output accumulate in fp32; in the first kernel the softmax
+ * weights are rounded to bf16 before the weighted sum of V.
+ *
+ *   max_group_size      host-side upper bound of the group sizes (> 0 when
+ *                       num_groups > 0; <= num_seqs)
+ *   max_shared_len      host-side upper bound of shared_lens;
+ *                       prefix_pt_stride * page_size >= max_shared_len.  A
+ *                       shared_len above it is a contract violation: the keys
+ *                       beyond the bound are then left out (no access leaves
+ *                       the page tables).  0 (or num_groups 0) runs the plain
+ *                       decode through kernels 2 and 3.
+ *   prefix_piece_keys   keys per piece of kernel 1: 0 = automatic
+ *                       (pa_cascade_piece_keys), else a positive multiple of
+ *                       64.
+ *   split_tokens        as for pa_decode.
+ *   workspace           >= pa_decode_cascade_workspace_bytes(...) bytes,
+ *                       256-byte aligned, clobbered.  Layout: fp32 partial
+ *                       outputs [num_seqs, num_q_heads, NP + S, head_dim],
+ *                       then (at a 256-byte boundary) fp32 log2-sum-exp
+ *                       values [num_seqs, num_q_heads, NP + S], where
+ *                       NP = ceil(max_shared_len / prefix_piece_keys) pieces
+ *                       of kernel 1 come first and S = ceil(max_seq_len /
+ *                       split_tokens) pieces of kernel 2 follow.
+ * bf16 pools only, head_dim 128 or 64, group size (num_q_heads /
+ * num_kv_heads) 1, 2, 4 or 8.  A request with seq_len 0 gets a zero row.
+ */
+int32_t pa_cascade_piece_keys(int32_t num_groups, int32_t max_group_size, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t max_shared_len);
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len, int32_t split_tokens,
+                                         int32_t num_groups, int32_t max_group_size, int32_t max_shared_len,
+                                         int32_t prefix_piece_keys);
+pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
+                            int32_t num_groups, int32_t max_group_size, const int32_t* prefix_page_table,
+                            int32_t prefix_pt_stride, const int32_t* shared_lens, int32_t max_shared_len,
+                            float scale, int32_t split_tokens, int32_t prefix_piece_keys, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_gather: copy the first seq_lens[b] tokens of every request, in logical

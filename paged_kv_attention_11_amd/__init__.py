@@ -68,6 +68,10 @@ SIGNATURES = {
     "pa_decode_partial": (_i32, _DECODE_ARGS),
     "pa_decode_combine": (_i32, _DECODE_ARGS),
     "pa_extend": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp]),
+    "pa_cascade_piece_keys": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_cascade_workspace_bytes": (_sz, [_i32] * 10),
+    "pa_decode_cascade": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32,
+                                 _vp, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pa_gather": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
 }
 
@@ -249,6 +253,55 @@ def extend(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, max_seq
                           page_table.shape[1], _ptr(seq_lens), B, int(max_q_len), int(max_seq_len),
                           float(scale), _ptr(out), _stream(stream))
     _check(st, "pa_extend")
+    return out
+
+
+def cascade_piece_keys(num_groups, max_group_size, num_q_heads, num_kv_heads, max_shared_len) -> int:
+    return load().pa_cascade_piece_keys(num_groups, max_group_size, num_q_heads, num_kv_heads, max_shared_len)
+
+
+def decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, num_groups,
+                                   max_group_size, max_shared_len, split_tokens=0, prefix_piece_keys=0) -> int:
+    return load().pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                    split_tokens, num_groups, max_group_size, max_shared_len,
+                                                    prefix_piece_keys)
+
+
+def decode_cascade(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, group_starts, max_group_size,
+                   prefix_page_table, shared_lens, max_shared_len, scale, out=None, workspace=None,
+                   split_tokens=0, prefix_piece_keys=0, stream=None):
+    """Decode of requests that share prefix pages: group j is requests
+    group_starts[j]..group_starts[j+1]-1, whose first shared_lens[b] keys sit
+    on prefix_page_table[j].  Same result as decode(...)."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16)
+    for t, n in ((page_table, "page_table"), (seq_lens, "seq_lens"), (group_starts, "group_starts"),
+                 (prefix_page_table, "prefix_page_table"), (shared_lens, "shared_lens")):
+        _dev(t, n, torch.int32)
+    if q.dim() != 3 or q.shape[2] != k_pool.shape[3]:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    B = q.shape[0]
+    if page_table.dim() != 2 or page_table.shape[0] != B or seq_lens.numel() != B or shared_lens.numel() != B:
+        raise ValueError("page_table [B, stride], seq_lens [B] and shared_lens [B] must match q")
+    ng = group_starts.numel() - 1
+    if ng < 0 or prefix_page_table.dim() != 2 or prefix_page_table.shape[0] != ng:
+        raise ValueError("group_starts [num_groups+1] and prefix_page_table [num_groups, stride] must agree")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if workspace is None:
+        nbytes = decode_cascade_workspace_bytes(B, q.shape[1], k_pool.shape[2], k_pool.shape[3], max_seq_len, ng,
+                                                max_group_size, max_shared_len, split_tokens, prefix_piece_keys)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    st = load().pa_decode_cascade(
+        ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,
+        int(max_seq_len), _ptr(group_starts), ng, int(max_group_size), _ptr(prefix_page_table),
+        prefix_page_table.shape[1], _ptr(shared_lens), int(max_shared_len), float(scale), int(split_tokens),
+        int(prefix_piece_keys), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "pa_decode_cascade")
     return out
 
 

@@ -113,11 +113,52 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   a.num_kv_heads = pool->num_kv_heads;
   a.head_dim = pool->head_dim;
   a.log2_page = ilog2(pool->page_size);
+  a.key_begin = nullptr;
   a.split_tokens = split;
   a.max_splits = (int32_t)S;
+  a.piece_offset = 0;
+  a.ws_pieces = (int32_t)S;
+  a.always_partial = 0;
+  a.group_lens = nullptr;
+  a.group_piece_keys = 1;
   a.bf16 = pool->dtype == PA_BF16;
   a.scale_log2 = scale * kLog2e;
   return PA_OK;
+}
+
+// Shared-prefix pass of the cascade decode: keys per piece.  Like the split
+// plan of the plain decode, it aims at about kTargetUnits work-groups.
+constexpr int kPrefixTile = 64;  // keys per tile of the matrix-core kernel
+constexpr int kPrefixRows = 128; // query rows per work-group of that kernel
+
+int64_t prefix_row_blocks(int32_t max_group_size, int32_t G) {
+  const int tok = kPrefixRows / G;
+  return (max_group_size + tok - 1) / tok;
+}
+
+int32_t auto_piece_keys(int32_t num_groups, int32_t max_group_size, int32_t G, int32_t num_kv_heads,
+                        int32_t max_shared_len) {
+  const int64_t units = (int64_t)num_groups * num_kv_heads * prefix_row_blocks(max_group_size, G);
+  if (units <= 0 || max_shared_len <= 0) return kPrefixTile;
+  const int64_t want = (kTargetUnits + units - 1) / units;
+  int64_t pk = (max_shared_len + want - 1) / want;
+  pk = (pk + kPrefixTile - 1) / kPrefixTile * kPrefixTile;
+  return (int32_t)(pk < kPrefixTile ? kPrefixTile : pk);
+}
+
+int32_t resolve_piece_keys(int32_t piece_keys, int32_t num_groups, int32_t max_group_size, int32_t G,
+                           int32_t num_kv_heads, int32_t max_shared_len) {
+  if (piece_keys == 0) return auto_piece_keys(num_groups, max_group_size, G, num_kv_heads, max_shared_len);
+  return (piece_keys > 0 && piece_keys % kPrefixTile == 0) ? piece_keys : -1;
+}
+
+// Workspace of the cascade decode: rows of (prefix pieces + suffix pieces).
+size_t cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                               int32_t split, int32_t max_shared_len, int32_t piece_keys) {
+  const int64_t S = (max_seq_len + split - 1) / split;
+  const int64_t NP = (max_shared_len + piece_keys - 1) / piece_keys;
+  const size_t rows = (size_t)num_seqs * num_q_heads * (S + NP);
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
 }
 
 }  // namespace
@@ -225,7 +266,7 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   if (num_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!q || !q_indptr || !page_table || !seq_lens || !out) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16)) return PA_ERR_SHAPE;
-  pa::ExtendArgs a;
+  pa::ExtendArgs a = {};
   a.k_pool = pool->k_pool;
   a.v_pool = pool->v_pool;
   a.q = q;
@@ -242,6 +283,127 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   a.max_q_len = max_q_len;
   a.scale_log2 = scale * kLog2e;
   return hip_status(pa::launch_extend(a, (hipStream_t)stream));
+}
+
+int32_t pa_cascade_piece_keys(int32_t num_groups, int32_t max_group_size, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t max_shared_len) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return kPrefixTile;
+  return auto_piece_keys(num_groups, max_group_size, num_q_heads / num_kv_heads, num_kv_heads,
+                         max_shared_len);
+}
+
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len, int32_t split_tokens,
+                                         int32_t num_groups, int32_t max_group_size, int32_t max_shared_len,
+                                         int32_t prefix_piece_keys) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      num_groups < 0 || max_group_size < 0 || max_shared_len < 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
+  const int32_t pk = resolve_piece_keys(prefix_piece_keys, num_groups, max_group_size,
+                                        num_q_heads / num_kv_heads, num_kv_heads, max_shared_len);
+  if (split < 0 || pk < 0) return 0;
+  return cascade_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, split, max_shared_len, pk);
+}
+
+pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
+                            int32_t num_groups, int32_t max_group_size, const int32_t* prefix_page_table,
+                            int32_t prefix_pt_stride, const int32_t* shared_lens, int32_t max_shared_len,
+                            float scale, int32_t split_tokens, int32_t prefix_piece_keys, void* out,
+                            void* workspace, size_t workspace_bytes_, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || max_seq_len < 0 || pt_stride < 0 || num_q_heads <= 0 || num_groups < 0 ||
+      max_group_size < 0 || prefix_pt_stride < 0 || max_shared_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
+  if ((int64_t)prefix_pt_stride * pool->page_size < max_shared_len) return PA_ERR_SHAPE;
+  if (max_group_size > num_seqs) return PA_ERR_SHAPE;
+  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
+  const int32_t pk = resolve_piece_keys(prefix_piece_keys, num_groups, max_group_size, G, pool->num_kv_heads,
+                                        max_shared_len);
+  if (split < 0 || pk < 0) return PA_ERR_SHAPE;
+  const int64_t S = (max_seq_len + split - 1) / split;
+  const int64_t NP = (max_shared_len + pk - 1) / pk;
+  if ((int64_t)num_seqs * pool->num_kv_heads * S > (int64_t)INT_MAX) return PA_ERR_SHAPE;
+  if ((int64_t)num_groups * pool->num_kv_heads * prefix_row_blocks(max_group_size, G) * NP > (int64_t)INT_MAX)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !page_table || !seq_lens || !out || !workspace) return PA_ERR_NULL;
+  const bool prefix_pass = num_groups > 0 && max_group_size > 0 && NP > 0;
+  if (prefix_pass && (!group_starts || !prefix_page_table || !shared_lens)) return PA_ERR_NULL;
+  if (!aligned(q, 16)) return PA_ERR_SHAPE;
+  const size_t need =
+      cascade_workspace_bytes(num_seqs, num_q_heads, pool->head_dim, max_seq_len, split, max_shared_len, pk);
+  if (workspace_bytes_ < need || !aligned(workspace, 256)) return PA_ERR_WORKSPACE;
+
+  const size_t rows = (size_t)num_seqs * num_q_heads * (S + NP);
+  float* o_part = (float*)workspace;
+  float* lse = (float*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float)));
+  const hipStream_t hs = (hipStream_t)stream;
+
+  // pass 1: each group's shared pages, all members' queries in one tile
+  if (prefix_pass) {
+    pa::ExtendArgs e = {};
+    e.k_pool = pool->k_pool;
+    e.v_pool = pool->v_pool;
+    e.q = q;
+    e.q_indptr = group_starts;
+    e.page_table = prefix_page_table;
+    e.seq_lens = shared_lens;
+    e.o_part = o_part;
+    e.lse = lse;
+    e.pt_stride = prefix_pt_stride;
+    e.num_seqs = num_groups;
+    e.num_q_heads = num_q_heads;
+    e.num_kv_heads = pool->num_kv_heads;
+    e.head_dim = pool->head_dim;
+    e.log2_page = ilog2(pool->page_size);
+    e.max_q_len = max_group_size;
+    e.max_keys = max_shared_len;
+    e.piece_keys = pk;
+    e.num_pieces = (int32_t)NP;
+    e.ws_pieces = (int32_t)(S + NP);
+    e.scale_log2 = scale * kLog2e;
+    st = hip_status(pa::launch_prefix(e, hs));
+    if (st != PA_OK) return st;
+  }
+
+  // pass 2: each request's own keys [shared_len, seq_len); pass 3: merge
+  pa::DecodeArgs a = {};
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.q = q;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.key_begin = prefix_pass ? shared_lens : nullptr;
+  a.o_part = o_part;
+  a.lse = lse;
+  a.out = out;
+  a.pt_stride = pt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.log2_page = ilog2(pool->page_size);
+  a.split_tokens = split;
+  a.max_splits = (int32_t)S;
+  a.piece_offset = (int32_t)NP;
+  a.ws_pieces = (int32_t)(S + NP);
+  a.always_partial = 1;
+  a.group_lens = prefix_pass ? shared_lens : nullptr;
+  a.group_piece_keys = pk;
+  a.bf16 = 1;
+  a.scale_log2 = scale * kLog2e;
+  st = hip_status(pa::launch_decode_partial(a, hs));
+  if (st != PA_OK) return st;
+  return hip_status(pa::launch_decode_combine(a, hs));
 }
 
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,

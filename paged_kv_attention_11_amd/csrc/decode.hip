@@ -137,18 +137,19 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   // (piece 0 exists for every request, the last pieces only for long ones),
   // and the requests that share prefix pages run close together in time on
   // the same XCD, where their common pages can be served from its L2.
-  const int S = p.max_splits;
   const int units = p.num_seqs * p.num_kv_heads;
   const int s = blockIdx.x / units;
   const int bg = blockIdx.x - s * units;
   const int g = bg % p.num_kv_heads;
   const int b = bg / p.num_kv_heads;
 
+  // This request's key range is [k0, L); piece s covers split_tokens of it.
   const int L = p.seq_lens[b];
-  const int t_begin = s * p.split_tokens;
+  const int k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
+  const int t_begin = k0 + s * p.split_tokens;
   if (t_begin >= L) return;  // uniform over the work-group
   const int n_tok = min(L - t_begin, p.split_tokens);
-  const int n_splits = (L + p.split_tokens - 1) / p.split_tokens;
+  const int n_splits = (L - k0 + p.split_tokens - 1) / p.split_tokens;
 
   // ---- stage the piece's key slots in LDS
   {
@@ -332,20 +333,23 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
       o = fmaf(f, s_acc[w][h][d], o);
     }
     o = o / lsum;
-    if (n_splits == 1) {
+    if (n_splits == 1 && !p.always_partial) {
       if constexpr (BF16)
         ((uint16_t*)p.out)[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
       else
         ((float*)p.out)[(row0 + h) * D + d] = o;
     } else {
-      const int64_t r = (row0 + h) * S + s;
+      const int64_t r = (row0 + h) * p.ws_pieces + p.piece_offset + s;
       p.o_part[r * D + d] = o;
       if (d == 0) p.lse[r] = M + __log2f(lsum);
     }
   }
 }
 
-// One wave per (request, query head): merge the request's pieces.
+// One wave per (request, query head): merge the request's pieces.  A row of
+// the workspace holds, at indices [0, ng), the pieces of the shared-prefix
+// pass (cascade decode only) and, from piece_offset on, the ns pieces of the
+// request's own key range; pieces with no visible key carry lse = -inf.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p) {
   constexpr int EPL = D / 64;  // output elements per lane
@@ -355,30 +359,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p)
   if (row >= rows) return;
   const int b = (int)(row / p.num_q_heads);
   const int L = p.seq_lens[b];
-  const int n = (L + p.split_tokens - 1) / p.split_tokens;
-  if (n == 1) return;  // written by the partial kernel
+  const int k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
+  // both counts are clamped to the pieces the workspace row holds
+  const int ns = min(max(L - k0 + p.split_tokens - 1, 0) / p.split_tokens, p.max_splits);
+  const int ng =
+      p.group_lens ? min((p.group_lens[b] + p.group_piece_keys - 1) / p.group_piece_keys, p.piece_offset) : 0;
+  if (ng == 0 && ns == 1 && !p.always_partial) return;  // written by the partial kernel
   float res[EPL];
-  if (n == 0) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) res[e] = 0.f;
-  } else {
-    const int S = p.max_splits;
-    const float* lse = p.lse + row * S;
+  for (int e = 0; e < EPL; ++e) res[e] = 0.f;
+  if (ng + ns > 0) {
+    const float* lse = p.lse + row * p.ws_pieces;
+    const float* op = p.o_part + row * p.ws_pieces * D + lane * EPL;
     float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, lse[s]);
+    for (int s = 0; s < ng; ++s) M = fmaxf(M, lse[s]);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[p.piece_offset + s]);
     float wsum = 0.f;
     float o[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-    const float* op = p.o_part + row * S * D + lane * EPL;
-    for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2(lse[s] - M);
+    auto add = [&](int s) {
+      const float l = lse[s];
+      if (l == -INFINITY) return;  // a piece with no visible key
+      const float w = fast_exp2(l - M);
       wsum += w;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = fmaf(w, op[(int64_t)s * D + e], o[e]);
-    }
+    };
+    for (int s = 0; s < ng; ++s) add(s);
+    for (int s = 0; s < ns; ++s) add(p.piece_offset + s);
+    if (wsum > 0.f) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) res[e] = o[e] / wsum;
+      for (int e = 0; e < EPL; ++e) res[e] = o[e] / wsum;
+    }
   }
   if constexpr (BF16) {
     uint16_t* out = (uint16_t*)p.out + row * D + lane * EPL;

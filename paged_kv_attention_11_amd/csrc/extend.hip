@@ -10,9 +10,15 @@
 //   request b, n_b new tokens after p_b cached keys; new token i (absolute
 //   position p_b + i) attends keys j <= p_b + i.
 //
+// The same kernel (PREFIX mode) computes the shared-prefix pass of the
+// cascade decode: its rows are the members of a request group times their
+// query heads, its keys the group's shared pages, and it writes split-softmax
+// partials that the decode combine kernel merges with each member's own keys.
+//
 // Design (FlashAttention-2 style tiling written for the CDNA4 matrix core):
-//  * Work-group = 4 waves = 128 query rows = (128 / G) tokens x all G query
-//    heads of one KV head, so every K/V tile staged in LDS serves G heads.
+//  * Work-group = 4 waves = 128 query rows = (128 / G) tokens (or group
+//    members) x all G query heads of one KV head, so every K/V tile staged in
+//    LDS serves G heads.
 //  * Per wave: 32 query rows.  Scores are computed transposed,
 //    S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in
 //    registers), so each lane owns one query row of the score tile and the
@@ -20,13 +26,11 @@
 //    also accumulated transposed, O^T += V^T P^T, so the rescale factor of a
 //    query row is lane-local and P goes from the score accumulator to the
 //    B operand without leaving registers.
-//  * K tile [64 keys][D] in LDS with 16-byte pieces XOR-swizzled by key; V
-//    tile stored transposed [D][64 keys] (transposed in registers on the way
-//    in), with the keys of each 16-key group in the order the score
-//    accumulator hands them to the B operand.  Two LDS buffers: the next
-//    tile's global loads are in flight while the current tile is computed.
+//  * K and V tiles (64 keys) are copied straight from the pages into a
+//    3-deep LDS ring with direct-to-LDS loads two tiles ahead; V stays in row
+//    layout and is read into the A operand with transposing LDS reads.
 //  * Key tiles entirely above the diagonal are never visited; only tiles that
-//    cross it are masked.
+//    cross it (or a row's key limit) are masked.
 //  * Softmax in fp32 (base 2, scale folded with log2 e); P is rounded to bf16
 //    for the matrix core; O accumulates in fp32 and is rounded once.
 #include "device.h"
@@ -112,52 +116,103 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* ptr) {
 
 constexpr float kExtRescaleSlack = 8.0f;  // log2 units, as in decode
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
+__device__ __forceinline__ int shfl_xor_i(int x, int mask) {
+  return __builtin_amdgcn_ds_bpermute((__lane_id() ^ mask) << 2, x);
+}
+
+// PREFIX = false: extend (chunk of new tokens, causal after the prefix).
+// PREFIX = true:  shared-prefix pass of the cascade decode.
+template <int D, int G, bool PREFIX>
+__global__ __launch_bounds__(kThreads) void mfma_attn_kernel(const ExtendArgs p) {
   using C = ExtCfg<D>;
-  constexpr int TOK = kRows / G;  // tokens per work-group
+  constexpr int TOK = kRows / G;  // tokens (or group members) per work-group
   constexpr int KSTEPS = C::KSTEPS, DT = C::DT, PPR = C::PPR, NDMA = C::NDMA;
 
   __shared__ uint4 s_k[kStages][kKT * PPR];
   __shared__ uint4 s_v[kStages][kKT * PPR];
   __shared__ int32_t s_pages[kPageCap];
+  __shared__ int32_t s_red[2][4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;  // query row within the wave
   const int half = lane >> 5;
-
-  // ---- work-group coordinates: the token blocks of one (request, KV head)
-  // are consecutive ids, heaviest (latest) first
-  const int qblocks = (p.max_q_len + TOK - 1) / TOK;
-  int bid = blockIdx.x;
-  const int qb = qblocks - 1 - (bid % qblocks);
-  bid /= qblocks;
-  const int g = bid % p.num_kv_heads;
-  const int b = bid / p.num_kv_heads;
-
-  const int r0 = p.q_indptr[b];
-  const int n = p.q_indptr[b + 1] - r0;
-  const int i0 = qb * TOK;
-  if (i0 >= n) return;
-  const int L = p.seq_lens[b];
-  const int prefix = L - n;
-  const int kv_len = prefix + min(i0 + TOK, n);  // keys this block can see
-  const int ntiles = (kv_len + kKT - 1) / kKT;
-
-  // ---- this lane's query row: rows are (head, token) with token fastest
-  const int row = wave * 32 + col;
+  const int row = wave * 32 + col;  // rows are (head, token/member) with token fastest
   const int hq = row / TOK;
-  const int ti = i0 + (row % TOK);
-  const bool qvalid = ti < n;
-  const int tmask = qvalid ? ti : (n - 1);  // padding rows mask like the last token
-  const int vis_lim = prefix + tmask;        // last visible key of this row
+
+  int g, q_row, vis_lim, k_begin, k_end, min_vis, piece = 0;
+  bool qvalid, has_keys;
+  const int32_t* pt;
+  if constexpr (!PREFIX) {
+    // work-group: token block qb of (request b, KV head g); the blocks of one
+    // (request, head) are consecutive ids, heaviest (latest) first
+    const int qblocks = (p.max_q_len + TOK - 1) / TOK;
+    int bid = blockIdx.x;
+    const int qb = qblocks - 1 - (bid % qblocks);
+    bid /= qblocks;
+    g = bid % p.num_kv_heads;
+    const int b = bid / p.num_kv_heads;
+    const int r0 = p.q_indptr[b];
+    const int n = p.q_indptr[b + 1] - r0;
+    const int i0 = qb * TOK;
+    if (i0 >= n) return;
+    const int prefix = p.seq_lens[b] - n;
+    k_begin = 0;
+    k_end = prefix + min(i0 + TOK, n);  // keys this block can see
+    const int ti = i0 + (row % TOK);
+    qvalid = ti < n;
+    q_row = r0 + ti;
+    vis_lim = prefix + (qvalid ? ti : (n - 1));  // padding rows mask like the last token
+    min_vis = prefix + i0;
+    has_keys = true;
+    pt = p.page_table + (int64_t)b * p.pt_stride;
+  } else {
+    // work-group: key piece sp of row block rb of (group j, KV head g)
+    const int rblocks = (p.max_q_len + TOK - 1) / TOK;
+    int bid = blockIdx.x;
+    piece = bid % p.num_pieces;
+    bid /= p.num_pieces;
+    const int rb = bid % rblocks;
+    bid /= rblocks;
+    g = bid % p.num_kv_heads;
+    const int j = bid / p.num_kv_heads;
+    const int m_begin = p.q_indptr[j];
+    const int gsize = p.q_indptr[j + 1] - m_begin;
+    const int m0 = rb * TOK;
+    if (m0 >= gsize) return;
+    const int mi = m0 + (row % TOK);
+    qvalid = mi < gsize;
+    q_row = m_begin + (qvalid ? mi : m0);
+    // clamped so that no key beyond the group's page-table rows is addressed
+    const int shared = qvalid ? min(p.seq_lens[q_row], p.max_keys) : 0;
+    vis_lim = shared - 1;
+    k_begin = piece * p.piece_keys;
+    has_keys = qvalid && shared > k_begin;
+    // block-wide largest and smallest key limits of the valid rows
+    int mx = qvalid ? shared : 0, mn = qvalid ? shared : 0x7fffffff;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      mx = max(mx, shfl_xor_i(mx, m));
+      mn = min(mn, shfl_xor_i(mn, m));
+    }
+    if (lane == 0) {
+      s_red[0][wave] = mx;
+      s_red[1][wave] = mn;
+    }
+    __syncthreads();
+    mx = max(max(s_red[0][0], s_red[0][1]), max(s_red[0][2], s_red[0][3]));
+    mn = min(min(s_red[1][0], s_red[1][1]), min(s_red[1][2], s_red[1][3]));
+    if (k_begin >= mx) return;  // no row of the block reads this piece (uniform)
+    k_end = min(k_begin + p.piece_keys, mx);
+    min_vis = mn - 1;
+    pt = p.page_table + (int64_t)j * p.pt_stride;
+  }
+  const int ntiles = (k_end - k_begin + kKT - 1) / kKT;
 
   uint4 qreg[KSTEPS];
   {
-    const uint16_t* qp =
-        (const uint16_t*)p.q + ((int64_t)(r0 + ti) * p.num_q_heads + (int64_t)g * G + hq) * D;
+    const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)q_row * p.num_q_heads + (int64_t)g * G + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
       qreg[ks] = qvalid ? *(const uint4*)(qp + ks * 16 + half * 8) : make_uint4(0, 0, 0, 0);
@@ -171,14 +226,13 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
     }
   }
 
-  const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride;
   const int sh = p.log2_page;
   const int pmask = (1 << sh) - 1;
   const int64_t row_stride = (int64_t)p.num_kv_heads * D;  // elements per slot
   const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)g * D;
   const int chunk_keys = kPageCap << sh;  // keys covered by one staging of page ids
-  const int npages = ((kv_len - 1) >> sh) + 1;
+  const int npages = ((k_end - 1) >> sh) + 1;
 
   // Page ids of chunk c (pages c*kPageCap ...) into LDS; entries past the
   // block's last page are not read.
@@ -197,13 +251,14 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
     for (int m = 0; m < NDMA; ++m) {
       const int blk = wave * NDMA + m;
       const int key = blk * C::RPB + lane / PPR;
-      const int kk = min(t * kKT + key, kv_len - 1);
+      const int kk = min(k_begin + t * kKT + key, k_end - 1);
       const int32_t page = s_pages[(kk >> sh) - chunk * kPageCap];
       const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride;
       dma16(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(key)) * 8);
       dma16(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(key)) * 8);
     }
   };
+  auto chunk_of = [&](int t) { return (k_begin + t * kKT) / chunk_keys; };
 
   f32x16_t o[DT];
 #pragma unroll
@@ -216,19 +271,33 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
   const float slack = kExtRescaleSlack / sl2;  // the same slack in raw-score units
 
   // ---- prologue: page ids, then tiles 0 and 1 in flight
-  int chunk = 0;
-  stage_pages(0);
+  int chunk = chunk_of(0);
+  stage_pages(chunk);
   __syncthreads();
-  issue_tile(0, 0, 0);
-  if (ntiles > 1) issue_tile(1, 1, 0);  // chunk_keys >= 1024, so tiles 0 and 1 share chunk 0
-  if (ntiles > 1) vm_wait<2 * NDMA>(); else vm_wait<0>();
+  issue_tile(0, 0, chunk);
+  if (ntiles > 1) {
+    if (chunk_of(1) != chunk) {  // rare: tile 1 starts the next chunk of page ids
+      vm_wait<0>();
+      __syncthreads();
+      chunk = chunk_of(1);
+      stage_pages(chunk);
+      __syncthreads();
+      issue_tile(1, 1, chunk);
+      vm_wait<2 * NDMA>();
+    } else {
+      issue_tile(1, 1, chunk);
+      vm_wait<2 * NDMA>();
+    }
+  } else {
+    vm_wait<0>();
+  }
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t % kStages;
     const bool ahead = (t + 2) < ntiles;
     if (ahead) {
-      const int c2 = ((t + 2) * kKT) / chunk_keys;
+      const int c2 = chunk_of(t + 2);
       if (c2 != chunk) {  // block-uniform and rare: restage page ids
         vm_wait<0>();
         __syncthreads();
@@ -253,9 +322,9 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
       }
     }
 
-    // ---- causal mask, only on tiles that cross the diagonal (block-uniform)
-    const int kt0 = t * kKT;
-    if (kt0 + kKT - 1 > prefix + i0) {
+    // ---- mask, only on tiles that reach past some row's last visible key
+    const int kt0 = k_begin + t * kKT;
+    if (kt0 + kKT - 1 > min_vis) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -274,8 +343,8 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
     if (__ballot(mx > m_ref + slack) != 0) {
-      const float m_new = fmaxf(m_ref, mx);  // finite: key 0 of tile 0 is visible to every row
-      const float alpha = fast_exp2((m_ref - m_new) * sl2);
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -283,7 +352,8 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     }
-    const float mb = -m_ref * sl2;
+    // a row with no visible key yet keeps weights exp2(-inf) = 0
+    const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
     uint4 pb[4];  // B operands of the four 16-key steps
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -299,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
     }
 
     // ---- O^T += V^T P^T; the A operand is read transposed out of row-major V:
-    // lane (group gq of 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims
+    // lane (group of 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims
     // d0 + 4(j%4) .. +3 and receives V[4 keys][d0 + j]
     {
       const int grp = lane >> 4, j = lane & 15;
@@ -307,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
         const int d = i * 32 + 16 * (grp & 1) + 4 * (j & 3);
-        const int lp = d >> 3;              // logical 16-byte piece
+        const int lp = d >> 3;               // logical 16-byte piece
         const int within = (d & 4) ? 8 : 0;  // byte offset inside the piece
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -328,38 +398,56 @@ __global__ __launch_bounds__(kThreads) void extend_kernel(const ExtendArgs p) {
 
   // ---- normalise and write this lane's row
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
-  if (!qvalid) return;
-  const float inv = 1.f / l_tot;
-  uint16_t* op = (uint16_t*)p.out + ((int64_t)(r0 + ti) * p.num_q_heads + (int64_t)g * G + hq) * D;
+  if constexpr (!PREFIX) {
+    if (!qvalid) return;
+    const float inv = 1.f / l_tot;
+    uint16_t* op = (uint16_t*)p.out + ((int64_t)q_row * p.num_q_heads + (int64_t)g * G + hq) * D;
 #pragma unroll
-  for (int i = 0; i < DT; ++i)
+    for (int i = 0; i < DT; ++i)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = i * 32 + 8 * q4 + 4 * half;
-      uint2 w;
-      w.x = pack2(o[i][4 * q4 + 0] * inv, o[i][4 * q4 + 1] * inv);
-      w.y = pack2(o[i][4 * q4 + 2] * inv, o[i][4 * q4 + 3] * inv);
-      *(uint2*)(op + d) = w;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = i * 32 + 8 * q4 + 4 * half;
+        uint2 w;
+        w.x = pack2(o[i][4 * q4 + 0] * inv, o[i][4 * q4 + 1] * inv);
+        w.y = pack2(o[i][4 * q4 + 2] * inv, o[i][4 * q4 + 3] * inv);
+        *(uint2*)(op + d) = w;
+      }
+  } else {
+    // the combine kernel reads this piece for a member only if the member
+    // has keys in it
+    if (!has_keys) return;
+    const float inv = 1.f / l_tot;
+    const int64_t wrow = ((int64_t)q_row * p.num_q_heads + (int64_t)g * G + hq) * p.ws_pieces + piece;
+    float* op = p.o_part + wrow * D;
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = i * 32 + 8 * q4 + 4 * half;
+        *(float4*)(op + d) = make_float4(o[i][4 * q4 + 0] * inv, o[i][4 * q4 + 1] * inv,
+                                         o[i][4 * q4 + 2] * inv, o[i][4 * q4 + 3] * inv);
+      }
+    if (half == 0) p.lse[wrow] = m_ref * sl2 + __log2f(l_tot);
+  }
 }
 
-template <int D, int G>
+template <int D, int G, bool PREFIX>
 hipError_t launch_g(const ExtendArgs& a, hipStream_t stream) {
   constexpr int TOK = kRows / G;
-  const int64_t qblocks = (a.max_q_len + TOK - 1) / TOK;
-  const int64_t blocks = qblocks * a.num_kv_heads * a.num_seqs;
+  const int64_t blocks_per = (a.max_q_len + TOK - 1) / TOK;
+  const int64_t blocks = blocks_per * a.num_kv_heads * a.num_seqs * (PREFIX ? a.num_pieces : 1);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((extend_kernel<D, G>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((mfma_attn_kernel<D, G, PREFIX>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool PREFIX>
 hipError_t launch_d(const ExtendArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_g<D, 1>(a, stream);
-    case 2: return launch_g<D, 2>(a, stream);
-    case 4: return launch_g<D, 4>(a, stream);
-    case 8: return launch_g<D, 8>(a, stream);
+    case 1: return launch_g<D, 1, PREFIX>(a, stream);
+    case 2: return launch_g<D, 2, PREFIX>(a, stream);
+    case 4: return launch_g<D, 4, PREFIX>(a, stream);
+    case 8: return launch_g<D, 8, PREFIX>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -367,8 +455,14 @@ hipError_t launch_d(const ExtendArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) return launch_d<128>(a, stream);
-  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  if (a.head_dim == 128) return launch_d<128, false>(a, stream);
+  if (a.head_dim == 64) return launch_d<64, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefix(const ExtendArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_d<128, true>(a, stream);
+  if (a.head_dim == 64) return launch_d<64, true>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -46,8 +46,9 @@ struct DecodeArgs {
   const void* q;
   const int32_t* page_table;
   const int32_t* seq_lens;
-  float* o_part;  // [B, Hq, S, D]
-  float* lse;     // [B, Hq, S], log2 domain
+  const int32_t* key_begin;  // [B] first key of each request's range, or null (0)
+  float* o_part;  // [B, Hq, ws_pieces, D]
+  float* lse;     // [B, Hq, ws_pieces], log2 domain
   void* out;      // [B, Hq, D]
   int64_t pt_stride;
   int32_t num_seqs;
@@ -56,26 +57,41 @@ struct DecodeArgs {
   int32_t head_dim;
   int32_t log2_page;
   int32_t split_tokens;
-  int32_t max_splits;
+  int32_t max_splits;    // pieces per request in the grid
+  int32_t piece_offset;  // workspace index of a request's piece 0
+  int32_t ws_pieces;     // pieces per (request, head) row of the workspace
+  int32_t always_partial;  // 1: never finish a single-piece request in the partial kernel
+  // leading pieces written by the shared-prefix kernel (combine only)
+  const int32_t* group_lens;  // [B] keys covered by those pieces, or null
+  int32_t group_piece_keys;
   int32_t bf16;
   float scale_log2;  // softmax scale * log2(e)
 };
 
+// Matrix-core attention tiles: the extend call, and the shared-prefix pass of
+// the cascade decode (rows = members of a request group x query heads, keys =
+// the group's shared pages, results written as split partials).
 struct ExtendArgs {
   const void* k_pool;
   const void* v_pool;
   const void* q;
-  const int32_t* q_indptr;
-  const int32_t* page_table;
-  const int32_t* seq_lens;
-  void* out;
+  const int32_t* q_indptr;     // extend: [B+1]; prefix: group starts [G+1]
+  const int32_t* page_table;   // extend: per request; prefix: per group
+  const int32_t* seq_lens;     // extend: [B]; prefix: shared lengths per request [B]
+  void* out;                   // extend: [T_q, Hq, D] bf16
+  float* o_part;               // prefix: decode workspace partials
+  float* lse;
   int64_t pt_stride;
-  int32_t num_seqs;
+  int32_t num_seqs;            // extend: requests; prefix: groups
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t log2_page;
-  int32_t max_q_len;
+  int32_t max_q_len;           // extend: longest chunk; prefix: largest group
+  int32_t max_keys;            // prefix: bound on the shared lengths (larger ones are clamped)
+  int32_t piece_keys;          // prefix: keys per piece
+  int32_t num_pieces;          // prefix: pieces per group
+  int32_t ws_pieces;           // prefix: workspace row stride in pieces
   float scale_log2;
 };
 
@@ -86,5 +102,6 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
+hipError_t launch_prefix(const ExtendArgs& a, hipStream_t stream);
 
 }  // namespace pa

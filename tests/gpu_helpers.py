@@ -37,6 +37,13 @@ def assert_close(got, ref, what, atol=ATOL, rtol=RTOL):
     return float(err.max()) if err.size else 0.0
 
 
+def bits(t):
+    """Raw bytes of a device tensor, for bit-for-bit comparisons."""
+    if t.dtype == torch().bfloat16:
+        return t.detach().cpu().view(torch().int16).numpy().tobytes()
+    return t.detach().cpu().numpy().tobytes()
+
+
 def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
@@ -75,3 +82,25 @@ def fresh(wl):
     pa().kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
     torch().cuda.synchronize()
     return dw
+
+
+def cascade_device(wl, starts=None, ppt=None, shl=None):
+    """Device copies of the group structure (the workload's own unless given)
+    and its host-side bounds: (group_starts, prefix_page_table, shared_lens,
+    max_group_size, max_shared_len)."""
+    if starts is None:
+        starts, ppt, shl = wl.cascade_inputs()
+    T = torch()
+    gmax = int((starts[1:] - starts[:-1]).max()) if len(starts) > 1 else 0
+    msh = int(shl.max()) if len(shl) else 0
+    return (T.from_numpy(np.ascontiguousarray(starts, np.int32)).cuda(),
+            T.from_numpy(np.ascontiguousarray(ppt, np.int32)).cuda(),
+            T.from_numpy(np.ascontiguousarray(shl, np.int32)).cuda(), gmax, msh)
+
+
+def gpu_cascade(wl, dw, split=0, piece_keys=0, groups=None, out=None):
+    gs, ppt, shl, gmax, msh = cascade_device(wl, *(groups or ()))
+    o = pa().decode_cascade(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, gs, gmax,
+                            ppt, shl, msh, wl.scale, out=out, split_tokens=split, prefix_piece_keys=piece_keys)
+    torch().cuda.synchronize()
+    return o

@@ -151,6 +151,54 @@ def test_extend_validation():
     assert extend(p, qmax=0) == OK
 
 
+def cascade(p, q=FAKE, Hq=32, pt=FAKE, stride=64, sl=FAKE, B=32, Lmax=1000, gs=FAKE, ng=2, gmax=16,
+            ppt=FAKE, pstride=8, shl=FAKE, msh=128, split=0, pk=0, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return pa.load().pa_decode_cascade(ctypes.byref(p), q, Hq, pt, stride, sl, B, Lmax, gs, ng, gmax, ppt,
+                                       pstride, shl, msh, 0.1, split, pk, out, ws, ws_bytes, None)
+
+
+def test_cascade_validation():
+    p = pool()
+    assert cascade(pool(dtype=0)) == DTYPE
+    assert cascade(p, Hq=24) == UNSUP  # group 3 has no matrix-core tile
+    assert cascade(p, Hq=30) == SHAPE
+    assert cascade(p, pstride=7) == SHAPE  # 7 * 16 < 128 shared keys
+    assert cascade(p, stride=10) == SHAPE
+    assert cascade(p, gmax=33) == SHAPE  # a group larger than the batch
+    assert cascade(p, ng=-1) == SHAPE
+    assert cascade(p, msh=-1) == SHAPE
+    assert cascade(p, pk=100) == SHAPE  # not a multiple of 64
+    assert cascade(p, pk=-64) == SHAPE
+    assert cascade(p, split=100) == SHAPE
+    assert cascade(p, gs=0) == NULL
+    assert cascade(p, ppt=0) == NULL
+    assert cascade(p, shl=0) == NULL
+    assert cascade(p, q=0) == NULL
+    assert cascade(p, ws=0) == NULL
+    assert cascade(p, ws=FAKE + 16) == WS
+    assert cascade(p, ws_bytes=4096) == WS
+    assert cascade(p, q=FAKE + 2) == SHAPE
+    assert cascade(p, B=0, gmax=0, ng=0, q=0, pt=0, sl=0, out=0, ws=0) == OK  # empty batch
+
+
+def test_cascade_plan_and_workspace():
+    lib = pa.load()
+    # 16 groups of 16 requests, 32/8 heads, 1024 shared keys: 16 x 8 x 1 row block
+    # units, 16 pieces each -> 64 keys per piece
+    assert lib.pa_cascade_piece_keys(16, 16, 32, 8, 1024) == 64
+    # one group, one KV head: 2048 pieces wanted, so pieces are the 64-key minimum
+    assert lib.pa_cascade_piece_keys(1, 4, 8, 1, 1000) == 64
+    # large groups of group-1 heads (128 rows per work-group): 2 row blocks
+    assert lib.pa_cascade_piece_keys(1, 200, 8, 8, 65536) == 64 * ((65536 // 128 + 63) // 64)
+    B, Hq, D, L, msh = 256, 32, 128, 8192, 1024
+    S, NP = 8, 16
+    rows = B * Hq * (S + NP)
+    expect = ((rows * D * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert lib.pa_decode_cascade_workspace_bytes(B, Hq, 8, D, L, 0, 16, 16, msh, 0) == expect
+    assert lib.pa_decode_cascade_workspace_bytes(B, Hq, 8, D, L, 0, 16, 16, msh, 96) == 0
+    assert lib.pa_decode_cascade_workspace_bytes(B, 30, 8, D, L, 0, 16, 16, msh, 0) == 0
+
+
 def test_gather_validation():
     p = pool()
     assert gather(p, ko=0) == NULL

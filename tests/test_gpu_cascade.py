@@ -1,0 +1,111 @@
+"""Cascade (prefix-aware) decode against the oracle's plain decode: reading a
+group's shared prefix pages once for all its members must not change the
+attention result (radix prefix sharing: nanoSGLang README, section
+Architecture; "mini-sglang from Scratch", section "What you will be able to
+do")."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import (assert_close, bits, f64, fresh, gpu_cascade, gpu_decode, named, stored_oracle_pools,
+                         torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def oracle_decode(wl, seqs=None):
+    kp, vp = stored_oracle_pools(wl)
+    sub = wl if seqs is None else wl.subset(seqs)
+    return oracle.decode(sub.q, kp, vp, sub.page_table, sub.seq_lens, wl.scale, wl.dtype)
+
+
+def test_cascade_matches_oracle_on_the_qwen3_8b_radix_workload():
+    name = "qwen3_8b_radix"
+    banner(f"cascade {name}")
+    wl, dw = named(name)
+    out = f64(gpu_cascade(wl, dw))
+    # two whole sharing groups, plus the shortest and longest requests
+    order = np.argsort(wl.seq_lens)
+    seqs = sorted(set(range(32)) | set(order[:3].tolist()) | set(order[-3:].tolist()))
+    err = assert_close(out[seqs], oracle_decode(wl, seqs), f"cascade {name}")
+    # every request against the plain decode of the same inputs
+    assert_close(out, f64(gpu_decode(wl, dw)), f"cascade vs decode {name}")
+    print(f"[result] cascade {name}: {len(seqs)} requests vs oracle, max abs err {err:.3g}", flush=True)
+
+
+CASCADE_SWEEP = [
+    # (lengths, Hq, Hkv, D, P, (group size, prefix pages), split, piece_keys)
+    ([700, 1200, 1500, 900, 1800, 2100, 513, 1025], 32, 8, 128, 16, (4, 64), 0, 0),
+    ([700, 1200, 1500, 900, 1800, 2100, 513, 1025], 32, 8, 128, 16, (4, 64), 128, 192),
+    ([5, 40, 17, 3000, 64, 65], 8, 2, 128, 16, (3, 8), 64, 64),        # short members, partial use
+    (list(range(1, 80)), 8, 2, 128, 16, (40, 4), 0, 0),                 # 40 members: two row blocks
+    (list(range(1, 80)), 16, 2, 128, 16, (40, 4), 64, 64),              # group 8: three row blocks
+    ([2000, 2100, 1, 4000], 4, 4, 128, 16, (2, 60), 0, 128),            # group 1
+    ([300, 301, 302, 900], 4, 2, 64, 16, (4, 16), 0, 0),                # group 2, D=64
+    ([3000, 2500, 2900, 1200], 8, 2, 128, 1, (4, 2048), 512, 2048),     # page size 1, page ids restaged
+    ([3000, 2500, 2900, 1200], 8, 2, 128, 1, (4, 2048), 0, 0),
+    ([1000, 1000, 1000], 64, 8, 128, 256, (3, 3), 0, 0),               # largest page
+    ([0, 5, 0, 40, 33], 8, 2, 128, 16, (5, 2), 0, 0),                   # empty requests in a group
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASCADE_SWEEP)))
+def test_cascade_sweep(case):
+    lens, Hq, Hkv, D, P, radix, split, pk = CASCADE_SWEEP[case]
+    banner(f"cascade sweep {case}: lens={lens[:8]} Hq={Hq} Hkv={Hkv} D={D} P={P} radix={radix} "
+           f"split={split} pk={pk}")
+    wl = W.make_custom(lens, Hq, Hkv, D, P, dtype="bf16", radix=radix, seed=300 + case)
+    dw = fresh(wl)
+    out = f64(gpu_cascade(wl, dw, split=split, piece_keys=pk))
+    assert_close(out, oracle_decode(wl), f"cascade sweep {case}")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b] == 0)
+
+
+def test_cascade_at_any_cut_inside_the_shared_pages():
+    """A member may declare any number of its shared keys as shared, also
+    mid-page and zero; the rest are read as its own keys."""
+    banner("cascade arbitrary cuts")
+    wl = W.make_custom([900, 1000, 1100, 1200, 700, 800, 1500, 1600], 32, 8, 128, 16, dtype="bf16",
+                       radix=(4, 40), seed=320)
+    dw = fresh(wl)
+    starts, ppt, shl = wl.cascade_inputs()
+    rng = np.random.default_rng(7)
+    cut = np.array([rng.integers(0, s + 1) for s in shl], np.int32)
+    cut[0], cut[5] = 0, shl[5]
+    out = f64(gpu_cascade(wl, dw, piece_keys=64, groups=(starts, ppt, cut)))
+    assert_close(out, oracle_decode(wl), "cascade with arbitrary cuts")
+
+
+def test_cascade_with_everything_shared():
+    """Singleton groups whose prefix table is the request's own: every key
+    goes through the matrix-core pass and the request's own pass is empty."""
+    banner("cascade all keys shared")
+    lens = [1, 63, 64, 65, 1000, 2047]
+    wl = W.make_custom(lens, 16, 4, 128, 16, dtype="bf16", seed=321)
+    dw = fresh(wl)
+    starts = np.arange(len(lens) + 1, dtype=np.int32)
+    out = f64(gpu_cascade(wl, dw, piece_keys=128, groups=(starts, wl.page_table, wl.seq_lens.astype(np.int32))))
+    assert_close(out, oracle_decode(wl), "cascade all shared")
+
+
+def test_cascade_without_sharing_is_the_plain_decode():
+    banner("cascade no sharing")
+    wl = W.make_custom([1, 17, 300, 1000, 2047], 32, 8, 128, 16, dtype="bf16", seed=322)
+    dw = fresh(wl)
+    out = gpu_cascade(wl, dw)
+    assert_close(f64(out), oracle_decode(wl), "cascade without sharing")
+
+
+def test_cascade_reruns_are_bit_identical():
+    banner("cascade determinism")
+    wl, dw = named("qwen3_8b_radix")
+    a = bits(gpu_cascade(wl, dw))
+    for _ in range(2):
+        assert bits(gpu_cascade(wl, dw)) == a

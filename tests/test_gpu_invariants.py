@@ -5,18 +5,13 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import assert_close, f64, fresh, gpu_decode, gpu_extend, named, pa, stored_oracle_pools, torch
+from gpu_helpers import assert_close, bits, f64, fresh, gpu_decode, gpu_extend, named, pa, stored_oracle_pools, torch
 
 pytestmark = pytest.mark.gpu
 
 
 def banner(msg):
     print(f"\n[case] {msg}", flush=True)
-
-
-def bits(t):
-    return t.detach().cpu().view(torch().int16).numpy().tobytes() if t.dtype == torch().bfloat16 \
-        else t.detach().cpu().numpy().tobytes()
 
 
 @pytest.mark.parametrize("name", ["qwen25_05b", "qwen3_06b_p1", "qwen3_8b_radix"])

@@ -109,6 +109,25 @@ class Workload:
     seed: int
     poison: Optional[str]
     shared_pages: Dict[int, np.ndarray] = field(default_factory=dict)  # group -> pages
+    group_size: int = 0  # requests per prefix-sharing group (0: no sharing)
+    shared_counts: Optional[np.ndarray] = None  # [B] leading pages each request reads from its group
+
+    def cascade_inputs(self):
+        """What an engine's prefix cache knows about the sharing: requests in
+        consecutive groups, each group's shared pages, and how many leading
+        keys of each request sit on them.  Returns (group_starts int32 [G+1],
+        prefix_page_table int32 [G, stride], shared_lens int32 [B])."""
+        B, P = self.num_seqs, self.page_size
+        if not self.group_size or self.shared_counts is None:
+            starts = np.arange(B + 1, dtype=np.int32)
+            return starts, np.zeros((B, 1), np.int32), np.zeros(B, np.int32)
+        ng = (B + self.group_size - 1) // self.group_size
+        starts = np.minimum(np.arange(ng + 1) * self.group_size, B).astype(np.int32)
+        stride = max(1, max(len(self.shared_pages[j]) for j in range(ng)))
+        ppt = np.zeros((ng, stride), np.int32)
+        for j in range(ng):
+            ppt[j, :len(self.shared_pages[j])] = self.shared_pages[j]
+        return starts, ppt, (self.shared_counts.astype(np.int64) * P).astype(np.int32)
 
     @property
     def group(self) -> int:
@@ -169,6 +188,7 @@ class Workload:
             k_new=self.k_new[rows], v_new=self.v_new[rows],
             slot_mapping=self.slot_mapping[rows], scale=self.scale, seed=self.seed,
             poison=self.poison, shared_pages=self.shared_pages,
+            group_size=0, shared_counts=None,
         )
 
 
@@ -188,7 +208,7 @@ def _assign_private(rng, seq_lens, P, num_pages):
             raise ValueError("pool too small for the drawn lengths")
         lists.append(perm[pos:pos + k].copy())
         pos += k
-    return lists, {}
+    return lists, {}, None
 
 
 def _assign_radix(rng, seq_lens, P, num_pages, group_size, prefix_pages):
@@ -202,7 +222,7 @@ def _assign_radix(rng, seq_lens, P, num_pages, group_size, prefix_pages):
     perm = rng.permutation(num_pages).astype(np.int32)
     shared = {g: perm[g * prefix_pages:(g + 1) * prefix_pages].copy() for g in range(ngroups)}
     pos = ngroups * prefix_pages
-    lists = []
+    lists, counts = [], []
     for b, L in enumerate(seq_lens):
         L = int(L)
         s = min(prefix_pages, max(0, (L - 1) // P)) if L > 0 else 0
@@ -210,8 +230,9 @@ def _assign_radix(rng, seq_lens, P, num_pages, group_size, prefix_pages):
         if pos + k > num_pages:
             raise ValueError("pool too small for the drawn lengths")
         lists.append(np.concatenate([shared[b // group_size][:s], perm[pos:pos + k]]).astype(np.int32))
+        counts.append(s)
         pos += k
-    return lists, shared
+    return lists, shared, np.array(counts, np.int32)
 
 
 # --------------------------------------------------------------------------
@@ -255,9 +276,9 @@ def build(
         raise ValueError("more new tokens than keys")
     # -- page assignment
     if radix is not None:
-        lists, shared = _assign_radix(rng, seq_lens, P, num_pages, *radix)
+        lists, shared, counts = _assign_radix(rng, seq_lens, P, num_pages, *radix)
     else:
-        lists, shared = _assign_private(rng, seq_lens, P, num_pages)
+        lists, shared, counts = _assign_private(rng, seq_lens, P, num_pages)
     max_pages = max([len(x) for x in lists] + [1])
     stride = max(stride or 0, max_pages)
     page_table = np.zeros((B, stride), np.int32)
@@ -284,7 +305,8 @@ def build(
                         q_indptr, page_table, lists, empty, empty,
                         np.zeros((0, num_q_heads, D), store_dt), np.zeros((0, Hkv, D), store_dt),
                         np.zeros((0, Hkv, D), store_dt), slot_mapping,
-                        float(np.float32(1.0 / math.sqrt(D))), seed, poison, shared)
+                        float(np.float32(1.0 / math.sqrt(D))), seed, poison, shared,
+                        radix[0] if radix else 0, counts)
     # -- pool contents: draws for every slot of every used page, in page-id order
     k_pool = np.zeros((num_pages, P, Hkv, D), store_dt)
     v_pool = np.zeros((num_pages, P, Hkv, D), store_dt)
@@ -307,7 +329,8 @@ def build(
             flat[~keep] = fill
     return Workload(name, kind, dtype, B, num_q_heads, Hkv, D, P, num_pages, seq_lens, n_new,
                     q_indptr, page_table, lists, k_pool, v_pool, q, k_new, v_new, slot_mapping,
-                    float(np.float32(1.0 / math.sqrt(D))), seed, poison, shared)
+                    float(np.float32(1.0 / math.sqrt(D))), seed, poison, shared,
+                    radix[0] if radix else 0, counts)
 
 
 # --------------------------------------------------------------------------

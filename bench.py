@@ -3,17 +3,21 @@
 
 One step = one decode layer-step of the Qwen3-8B-shaped batch with radix
 prefix sharing (256 requests, log-uniform lengths 512..8192, 32 query / 8 KV
-heads, head_dim 128, page 16, bf16): kv_store of the 256 new K/V rows, then
-paged decode (partial kernel + combine kernel).  Inputs are resident in HBM
-before timing starts.  The chunked-prefill extend call (8 requests, prefix
-0..4096 + 512-token chunk, same head shape) is timed in the same run and
-reported in its own object.
+heads, head_dim 128, page 16, bf16; groups of 16 requests share a 1024-token
+prefix): kv_store of the 256 new K/V rows, then the cascade decode (shared
+prefix pass on the matrix cores, each request's own keys through the split-K
+decode kernel, combine).  Inputs are resident in HBM before timing starts.
+The plain decode (partial + combine over every request's whole page list) and
+the chunked-prefill extend call (8 requests, prefix 0..4096 + 512-token
+chunk, same head shape) are timed in the same run and reported in their own
+objects.
 
 Prints one JSON line.  `value` is decode KV throughput in GB/s counted on the
 distinct KV bytes the step must read (each physical slot once); `roofline`
-describes the dominant kernel (the decode partial kernel) with its average
-duration taken from HIP events on the launch stream; `cpu_baseline` is the
-CPU oracle timed on a bounded sample of the same workload.
+describes the dominant kernel (the split-K decode kernel over the requests'
+own keys) with its average duration taken from HIP events on the launch
+stream; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -30,7 +34,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_partial_qwen3_8b_radix_counters.txt")
+PROFILE_COUNTERS = {
+    "cascade": os.path.join(ROOT, "profiles", "decode_partial_own_keys_qwen3_8b_radix_counters.txt"),
+    "plain": os.path.join(ROOT, "profiles", "decode_partial_qwen3_8b_radix_counters.txt"),
+}
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_attention_11_amd", "csrc", f)
                   for f in ("decode.hip", "device.h", "internal.h")]
 
@@ -44,6 +51,9 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extend", action="store_true")
+    ap.add_argument("--no-plain", action="store_true", help="skip the plain-decode comparison")
+    ap.add_argument("--path", choices=["cascade", "plain"], default="cascade",
+                    help="decode path of the timed step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU leg")
     ap.add_argument("--copy-only", action="store_true",
                     help="only the plain-copy calibration (for hardware-counter scaling runs)")
@@ -62,13 +72,14 @@ def sources_digest(paths):
     return h.hexdigest()[:16]
 
 
-def read_traffic(launch_units):
-    """HBM bytes per partial-kernel launch from the committed counter summary,
-    if it was taken on the current kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
+def read_traffic(path):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    fname = PROFILE_COUNTERS[path]
+    if not os.path.exists(fname):
         return None
     kv = {}
-    for line in open(PROFILE_COUNTERS):
+    for line in open(fname):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -182,33 +193,53 @@ def main():
                                                "launch_ms": round(ms, 4)}}), flush=True)
         return
 
-    # ---------------- decode step: store + partial + combine
+    # ---------------- decode step
     t0 = time.perf_counter()
     wl = W.make(args.config)
     log(f"generated {args.config} in {time.perf_counter() - t0:.1f}s")
     dw = W.to_device(wl)
     B, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    P = wl.page_size
     split = args.split_tokens or pa.decode_split_tokens(B, Hkv, wl.max_seq_len)
     out = torch.empty_like(dw.q)
-    ws = pa.decode_workspace(dw.q, dw.k_pool, wl.max_seq_len, split)
     stream = torch.cuda.current_stream()
+    starts, ppt, shl = wl.cascade_inputs()
+    gmax = int((starts[1:] - starts[:-1]).max()) if B else 0
+    msh = int(shl.max()) if B else 0
+    cascade = args.path == "cascade"
+    if cascade:
+        gs_d = torch.from_numpy(starts).cuda()
+        ppt_d = torch.from_numpy(ppt).cuda()
+        shl_d = torch.from_numpy(shl).cuda()
+        piece_keys = pa.cascade_piece_keys(len(starts) - 1, gmax, Hq, Hkv, msh)
+        nb = pa.decode_cascade_workspace_bytes(B, Hq, Hkv, D, wl.max_seq_len, len(starts) - 1, gmax, msh, split)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+        stages = ["prefix", "suffix", "combine"]
+
+        def call(stage):
+            pa.decode_cascade(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, gs_d, gmax,
+                              ppt_d, shl_d, msh, wl.scale, out=out, workspace=ws, split_tokens=split, stage=stage)
+    else:
+        ws = pa.decode_workspace(dw.q, dw.k_pool, wl.max_seq_len, split)
+        stages = ["partial", "combine"]
+
+        def call(stage):
+            fn = pa.decode_partial if stage == "partial" else pa.decode_combine
+            fn(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, wl.scale, out, ws, split)
 
     def step(ev=None):
         pa.kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
+        for i, stage in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            call(stage)
         if ev is not None:
-            ev[0].record(stream)
-        pa.decode_partial(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, wl.scale,
-                          out, ws, split)
-        if ev is not None:
-            ev[1].record(stream)
-        pa.decode_combine(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, wl.scale,
-                          out, ws, split)
+            ev[len(stages)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -220,17 +251,33 @@ def main():
     wall = time.perf_counter() - w0
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    log(f"decode: {ms_step * 1e3:.1f} us/step, partial {partial_ms * 1e3:.1f} us (wall {wall:.3f}s)")
+    stage_ms = {st: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, st in enumerate(stages)}
+    log(f"decode ({args.path}): {ms_step * 1e3:.1f} us/step; " +
+        ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in stage_ms.items()) + f" (wall {wall:.3f}s)")
 
     kv_unique = wl.kv_bytes_unique()
     kv_logical = wl.kv_bytes_logical()
-    P = wl.page_size
-    pt_bytes = 4 * int(sum((int(L) + P - 1) // P for L in wl.seq_lens))
+    slot_bytes = 2 * Hkv * D * wl.elem_bytes
     q_bytes = B * Hq * D * wl.elem_bytes
-    partial_alg_bytes = kv_unique + q_bytes + pt_bytes + 4 * B  # per partial launch
-    achieved = partial_alg_bytes / (partial_ms * 1e-3) / 1e9
-    traffic = read_traffic(1)
+    if cascade:
+        # the split-K kernel reads each request's own keys [shared_len, seq_len): distinct slots
+        own = set()
+        pages_read = 0
+        for b in range(B):
+            L, s0 = int(wl.seq_lens[b]), int(shl[b])
+            if L > s0:
+                pl = wl.page_table[b]
+                t = np.arange(s0, L)
+                own.update((pl[t // P].astype(np.int64) * P + t % P).tolist())
+                pages_read += (L - 1) // P - s0 // P + 1
+        dom_kernel, dom_ms = "decode_partial_kernel<bf16, D=128, G=4> (own keys)", stage_ms["suffix"]
+        dom_bytes = len(own) * slot_bytes + q_bytes + 4 * pages_read + 8 * B
+    else:
+        pages_read = int(sum((int(L) + P - 1) // P for L in wl.seq_lens))
+        dom_kernel, dom_ms = "decode_partial_kernel<bf16, D=128, G=4>", stage_ms["partial"]
+        dom_bytes = kv_unique + q_bytes + 4 * pages_read + 4 * B
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.path)
     value = kv_unique / (ms_step * 1e-3) / 1e9
 
     result = {
@@ -251,30 +298,63 @@ def main():
             "description": W.DESCRIPTIONS.get(args.config, args.config),
             "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
             "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "split_tokens": split,
-            "step": "kv_store + decode_partial + decode_combine",
+            "step": "kv_store + " + ("decode_cascade (prefix, suffix, combine)" if cascade
+                                     else "decode_partial + decode_combine"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "kv_bytes_unique": kv_unique,
         "kv_bytes_logical": kv_logical,
-        "logical_kv_GBps": round(kv_logical / (ms_step * 1e-3) / 1e9, 2),
-        "partial_kernel_us": round(partial_ms * 1e3, 2),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "roofline": {
-            "kernel": "decode_partial_kernel<bf16, D=128, G=4>",
+            "kernel": dom_kernel,
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": partial_alg_bytes,
+            "algorithmic_bytes_per_launch": dom_bytes,
         },
         "device": dev_name,
     }
+    if cascade:
+        result["config"]["prefix_piece_keys"] = piece_keys
+        result["config"]["groups"] = len(starts) - 1
+
+    # ---------------- plain decode of the same step, for comparison
+    if cascade and not args.no_plain:
+        del ws
+        pws = pa.decode_workspace(dw.q, dw.k_pool, wl.max_seq_len, split)
+        pout = torch.empty_like(dw.q)
+
+        def plain():
+            pa.kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
+            pa.decode(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, wl.scale, pout, pws,
+                      split)
+
+        for _ in range(max(3, args.warmup // 2)):
+            plain()
+        torch.cuda.synchronize()
+        ps, pe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ksteps = max(5, args.steps // 2)
+        ps.record(stream)
+        for _ in range(ksteps):
+            plain()
+        pe.record(stream)
+        torch.cuda.synchronize()
+        pms = ps.elapsed_time(pe) / ksteps
+        result["plain_decode"] = {
+            "step": "kv_store + decode (partial + combine over whole page lists)",
+            "ms_per_step": round(pms, 5),
+            "GBps_unique": round(kv_unique / (pms * 1e-3) / 1e9, 2),
+            "decode_tokens_per_s": round(B / (pms * 1e-3), 1),
+        }
+        log(f"plain decode: {pms * 1e3:.1f} us/step")
+        del pws
 
     # ---------------- extend (chunked prefill on the same head shape)
     if not args.no_extend:
-        del ws
         ew = W.make("qwen3_8b_extend")
         edw = W.to_device(ew)
         eout = torch.empty_like(edw.q)

@@ -249,6 +249,37 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The three kernels of pa_decode_cascade, callable one at a time in this
+ * order (same arguments; each validates them all).  _prefix enqueues kernel
+ * 1 (nothing when there is no prefix pass), _suffix kernel 2, _combine
+ * kernel 3.
+ */
+pa_status pa_decode_cascade_prefix(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                                   const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
+                                   int32_t num_groups, int32_t max_group_size,
+                                   const int32_t* prefix_page_table, int32_t prefix_pt_stride,
+                                   const int32_t* shared_lens, int32_t max_shared_len, float scale,
+                                   int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+pa_status pa_decode_cascade_suffix(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                                   const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
+                                   int32_t num_groups, int32_t max_group_size,
+                                   const int32_t* prefix_page_table, int32_t prefix_pt_stride,
+                                   const int32_t* shared_lens, int32_t max_shared_len, float scale,
+                                   int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                                    int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
+                                    int32_t num_groups, int32_t max_group_size,
+                                    const int32_t* prefix_page_table, int32_t prefix_pt_stride,
+                                    const int32_t* shared_lens, int32_t max_shared_len, float scale,
+                                    int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * pa_gather: copy the first seq_lens[b] tokens of every request, in logical
  * order, to contiguous k_out / v_out rows starting at row out_offsets[b]
  * (int64 [num_seqs + 1], device).  k_out, v_out: [out_offsets[num_seqs],

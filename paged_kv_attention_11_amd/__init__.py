@@ -57,6 +57,9 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 _POOLP = ctypes.POINTER(KVPool)
 _DECODE_ARGS = [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]
 
+_CASCADE_ARGS = [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
+                 _i32, _vp, _vp, _sz, _vp]
+
 SIGNATURES = {
     # name: (restype, argtypes) -- mirrors include/pagedattn.h
     "pa_version": (ctypes.c_char_p, []),
@@ -70,8 +73,10 @@ SIGNATURES = {
     "pa_extend": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp]),
     "pa_cascade_piece_keys": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_cascade_workspace_bytes": (_sz, [_i32] * 10),
-    "pa_decode_cascade": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32,
-                                 _vp, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "pa_decode_cascade": (_i32, _CASCADE_ARGS),
+    "pa_decode_cascade_prefix": (_i32, _CASCADE_ARGS),
+    "pa_decode_cascade_suffix": (_i32, _CASCADE_ARGS),
+    "pa_decode_cascade_combine": (_i32, _CASCADE_ARGS),
     "pa_gather": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
 }
 
@@ -269,10 +274,11 @@ def decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim
 
 def decode_cascade(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, group_starts, max_group_size,
                    prefix_page_table, shared_lens, max_shared_len, scale, out=None, workspace=None,
-                   split_tokens=0, prefix_piece_keys=0, stream=None):
+                   split_tokens=0, prefix_piece_keys=0, stream=None, stage=None):
     """Decode of requests that share prefix pages: group j is requests
     group_starts[j]..group_starts[j+1]-1, whose first shared_lens[b] keys sit
-    on prefix_page_table[j].  Same result as decode(...)."""
+    on prefix_page_table[j].  Same result as decode(...).  `stage` ("prefix",
+    "suffix" or "combine") enqueues only that kernel."""
     torch = _torch()
     pool = make_pool(k_pool, v_pool)
     _dev(q, "q", torch.bfloat16)
@@ -295,13 +301,16 @@ def decode_cascade(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, group_s
                                                 max_group_size, max_shared_len, split_tokens, prefix_piece_keys)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace")
-    st = load().pa_decode_cascade(
+    fn = "pa_decode_cascade" + ("" if stage is None else "_" + stage)
+    if fn not in SIGNATURES:
+        raise ValueError(f"unknown cascade stage {stage!r}")
+    st = getattr(load(), fn)(
         ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,
         int(max_seq_len), _ptr(group_starts), ng, int(max_group_size), _ptr(prefix_page_table),
         prefix_page_table.shape[1], _ptr(shared_lens), int(max_shared_len), float(scale), int(split_tokens),
         int(prefix_piece_keys), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
-    _check(st, "pa_decode_cascade")
+    _check(st, fn)
     return out
 
 

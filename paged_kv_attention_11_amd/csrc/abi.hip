@@ -126,10 +126,15 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   return PA_OK;
 }
 
-// Shared-prefix pass of the cascade decode: keys per piece.  Like the split
-// plan of the plain decode, it aims at about kTargetUnits work-groups.
-constexpr int kPrefixTile = 64;  // keys per tile of the matrix-core kernel
-constexpr int kPrefixRows = 128; // query rows per work-group of that kernel
+// Shared-prefix pass of the cascade decode: keys per piece.  A work-group of
+// the matrix-core kernel holds a 96 KB LDS ring, so one runs per compute unit
+// and a tile costs about the same however many work-groups wait: the plan
+// aims at one work-group per compute unit, each looping over its piece's
+// tiles, rather than many short work-groups that each pay the prologue and
+// write partials.
+constexpr int kPrefixTile = 64;   // keys per tile of the matrix-core kernel
+constexpr int kPrefixRows = 128;  // query rows per work-group of that kernel
+constexpr int64_t kPrefixTargetUnits = 256;
 
 int64_t prefix_row_blocks(int32_t max_group_size, int32_t G) {
   const int tok = kPrefixRows / G;
@@ -140,7 +145,7 @@ int32_t auto_piece_keys(int32_t num_groups, int32_t max_group_size, int32_t G, i
                         int32_t max_shared_len) {
   const int64_t units = (int64_t)num_groups * num_kv_heads * prefix_row_blocks(max_group_size, G);
   if (units <= 0 || max_shared_len <= 0) return kPrefixTile;
-  const int64_t want = (kTargetUnits + units - 1) / units;
+  const int64_t want = (kPrefixTargetUnits + units - 1) / units;
   int64_t pk = (max_shared_len + want - 1) / want;
   pk = (pk + kPrefixTile - 1) / kPrefixTile * kPrefixTile;
   return (int32_t)(pk < kPrefixTile ? kPrefixTile : pk);
@@ -306,13 +311,20 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
   return cascade_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, split, max_shared_len, pk);
 }
 
-pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
-                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
-                            int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
-                            int32_t num_groups, int32_t max_group_size, const int32_t* prefix_page_table,
-                            int32_t prefix_pt_stride, const int32_t* shared_lens, int32_t max_shared_len,
-                            float scale, int32_t split_tokens, int32_t prefix_piece_keys, void* out,
-                            void* workspace, size_t workspace_bytes_, void* stream) {
+}  // extern "C"
+
+namespace {
+
+enum : unsigned { kStagePrefix = 1, kStageSuffix = 2, kStageCombine = 4, kStageAll = 7 };
+
+// The cascade decode's validation, plan and the enqueueing of the selected
+// stages (all three for pa_decode_cascade).
+pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* page_table,
+                       int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                       const int32_t* group_starts, int32_t num_groups, int32_t max_group_size,
+                       const int32_t* prefix_page_table, int32_t prefix_pt_stride, const int32_t* shared_lens,
+                       int32_t max_shared_len, float scale, int32_t split_tokens, int32_t prefix_piece_keys,
+                       void* out, void* workspace, size_t workspace_bytes_, void* stream, unsigned stages) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
@@ -349,7 +361,7 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
   const hipStream_t hs = (hipStream_t)stream;
 
   // pass 1: each group's shared pages, all members' queries in one tile
-  if (prefix_pass) {
+  if (prefix_pass && (stages & kStagePrefix)) {
     pa::ExtendArgs e = {};
     e.k_pool = pool->k_pool;
     e.v_pool = pool->v_pool;
@@ -401,10 +413,36 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
   a.group_piece_keys = pk;
   a.bf16 = 1;
   a.scale_log2 = scale * kLog2e;
-  st = hip_status(pa::launch_decode_partial(a, hs));
-  if (st != PA_OK) return st;
-  return hip_status(pa::launch_decode_combine(a, hs));
+  if (stages & kStageSuffix) {
+    st = hip_status(pa::launch_decode_partial(a, hs));
+    if (st != PA_OK) return st;
+  }
+  if (stages & kStageCombine) return hip_status(pa::launch_decode_combine(a, hs));
+  return PA_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+#define PA_CASCADE_PARAMS                                                                                   \
+  const pa_kv_pool *pool, const void *q, int32_t num_q_heads, const int32_t *page_table, int32_t pt_stride, \
+      const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, const int32_t *group_starts,          \
+      int32_t num_groups, int32_t max_group_size, const int32_t *prefix_page_table, int32_t prefix_pt_stride, \
+      const int32_t *shared_lens, int32_t max_shared_len, float scale, int32_t split_tokens,                 \
+      int32_t prefix_piece_keys, void *out, void *workspace, size_t workspace_bytes_, void *stream
+#define PA_CASCADE_ARGS                                                                                    \
+  pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs, max_seq_len, group_starts, num_groups, \
+      max_group_size, prefix_page_table, prefix_pt_stride, shared_lens, max_shared_len, scale, split_tokens, \
+      prefix_piece_keys, out, workspace, workspace_bytes_, stream
+
+pa_status pa_decode_cascade(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStageAll); }
+pa_status pa_decode_cascade_prefix(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStagePrefix); }
+pa_status pa_decode_cascade_suffix(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStageSuffix); }
+pa_status pa_decode_cascade_combine(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStageCombine); }
+
+#undef PA_CASCADE_PARAMS
+#undef PA_CASCADE_ARGS
 
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
                     const int32_t* seq_lens, const int64_t* out_offsets, int32_t num_seqs,

@@ -349,10 +349,14 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
 // One wave per (request, query head): merge the request's pieces.  A row of
 // the workspace holds, at indices [0, ng), the pieces of the shared-prefix
 // pass (cascade decode only) and, from piece_offset on, the ns pieces of the
-// request's own key range; pieces with no visible key carry lse = -inf.
+// request's own key range.  The log-sum-exp values of up to 64 pieces are
+// read at once (one per lane), and the partial outputs in batches of eight
+// independent loads, so the merge costs a few memory latencies, not one per
+// piece.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p) {
   constexpr int EPL = D / 64;  // output elements per lane
+  constexpr int BATCH = 8;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
@@ -365,30 +369,58 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p)
   const int ng =
       p.group_lens ? min((p.group_lens[b] + p.group_piece_keys - 1) / p.group_piece_keys, p.piece_offset) : 0;
   if (ng == 0 && ns == 1 && !p.always_partial) return;  // written by the partial kernel
+  const int n = ng + ns;
+  const int off = p.piece_offset - ng;  // merged piece i >= ng sits at workspace index i + off
+  const float* lse = p.lse + row * p.ws_pieces;
+  const float* op = p.o_part + row * p.ws_pieces * D + lane * EPL;
+
   float res[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) res[e] = 0.f;
-  if (ng + ns > 0) {
-    const float* lse = p.lse + row * p.ws_pieces;
-    const float* op = p.o_part + row * p.ws_pieces * D + lane * EPL;
+  if (n > 0) {
+    // pieces with no visible key (lse = -inf) get weight zero
     float M = -INFINITY;
-    for (int s = 0; s < ng; ++s) M = fmaxf(M, lse[s]);
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[p.piece_offset + s]);
-    float wsum = 0.f;
+    for (int c = 0; c < n; c += 64) {
+      const int i = min(c + lane, n - 1);
+      M = fmaxf(M, lse[i < ng ? i : i + off]);
+    }
+    M = wave_max(M);
     float o[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-    auto add = [&](int s) {
-      const float l = lse[s];
-      if (l == -INFINITY) return;  // a piece with no visible key
-      const float w = fast_exp2(l - M);
-      wsum += w;
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+      for (int c = 0; c < n; c += 64) {
+        const int i = min(c + lane, n - 1);
+        const float l = lse[i < ng ? i : i + off];
+        const float w = (c + lane < n && l != -INFINITY) ? fast_exp2(l - M) : 0.f;
+        wsum += w;
+        const int cnt = min(64, n - c);
+        for (int j0 = 0; j0 < cnt; j0 += BATCH) {
+          float wk[BATCH], v[BATCH][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(w, op[(int64_t)s * D + e], o[e]);
-    };
-    for (int s = 0; s < ng; ++s) add(s);
-    for (int s = 0; s < ns; ++s) add(p.piece_offset + s);
-    if (wsum > 0.f) {
+          for (int k = 0; k < BATCH; ++k) {
+            const int j = min(j0 + k, cnt - 1);  // clamped: a real piece, weight zero below
+            const int pi = c + j;
+            const float* src = op + (int64_t)(pi < ng ? pi : pi + off) * D;
+            wk[k] = j0 + k < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
+                                 : 0.f;
+            if constexpr (EPL == 2) {
+              const float2 x = *(const float2*)src;
+              v[k][0] = x.x;
+              v[k][1] = x.y;
+            } else {
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) v[k][e] = src[e];
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = wk[k] > 0.f ? fmaf(wk[k], v[k][e], o[e]) : o[e];
+        }
+      }
+      wsum = wave_sum(wsum);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) res[e] = o[e] / wsum;
     }

@@ -152,13 +152,17 @@ def test_extend_validation():
 
 
 def cascade(p, q=FAKE, Hq=32, pt=FAKE, stride=64, sl=FAKE, B=32, Lmax=1000, gs=FAKE, ng=2, gmax=16,
-            ppt=FAKE, pstride=8, shl=FAKE, msh=128, split=0, pk=0, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
-    return pa.load().pa_decode_cascade(ctypes.byref(p), q, Hq, pt, stride, sl, B, Lmax, gs, ng, gmax, ppt,
-                                       pstride, shl, msh, 0.1, split, pk, out, ws, ws_bytes, None)
+            ppt=FAKE, pstride=8, shl=FAKE, msh=128, split=0, pk=0, out=FAKE, ws=FAKE, ws_bytes=1 << 40,
+            fn="pa_decode_cascade"):
+    return getattr(pa.load(), fn)(ctypes.byref(p), q, Hq, pt, stride, sl, B, Lmax, gs, ng, gmax, ppt,
+                                  pstride, shl, msh, 0.1, split, pk, out, ws, ws_bytes, None)
 
 
-def test_cascade_validation():
+@pytest.mark.parametrize("fn", ["pa_decode_cascade", "pa_decode_cascade_prefix", "pa_decode_cascade_suffix",
+                                "pa_decode_cascade_combine"])
+def test_cascade_validation(fn):
     p = pool()
+    cascade = lambda *a, **k: globals()["cascade"](*a, fn=fn, **k)
     assert cascade(pool(dtype=0)) == DTYPE
     assert cascade(p, Hq=24) == UNSUP  # group 3 has no matrix-core tile
     assert cascade(p, Hq=30) == SHAPE
@@ -183,15 +187,15 @@ def test_cascade_validation():
 
 def test_cascade_plan_and_workspace():
     lib = pa.load()
-    # 16 groups of 16 requests, 32/8 heads, 1024 shared keys: 16 x 8 x 1 row block
-    # units, 16 pieces each -> 64 keys per piece
-    assert lib.pa_cascade_piece_keys(16, 16, 32, 8, 1024) == 64
-    # one group, one KV head: 2048 pieces wanted, so pieces are the 64-key minimum
+    # one work-group per compute unit (256): 16 groups of 16 requests, 32/8 heads,
+    # 1024 shared keys -> 16 x 8 x 1 row block units, 2 pieces each of 512 keys
+    assert lib.pa_cascade_piece_keys(16, 16, 32, 8, 1024) == 512
+    # one group, one KV head: 256 pieces wanted, so pieces are the 64-key minimum
     assert lib.pa_cascade_piece_keys(1, 4, 8, 1, 1000) == 64
     # large groups of group-1 heads (128 rows per work-group): 2 row blocks
-    assert lib.pa_cascade_piece_keys(1, 200, 8, 8, 65536) == 64 * ((65536 // 128 + 63) // 64)
+    assert lib.pa_cascade_piece_keys(1, 200, 8, 8, 65536) == 65536 // 16
     B, Hq, D, L, msh = 256, 32, 128, 8192, 1024
-    S, NP = 8, 16
+    S, NP = 8, 2
     rows = B * Hq * (S + NP)
     expect = ((rows * D * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert lib.pa_decode_cascade_workspace_bytes(B, Hq, 8, D, L, 0, 16, 16, msh, 0) == expect

@@ -109,3 +109,22 @@ def test_cascade_reruns_are_bit_identical():
     a = bits(gpu_cascade(wl, dw))
     for _ in range(2):
         assert bits(gpu_cascade(wl, dw)) == a
+
+
+def test_cascade_stages_called_one_at_a_time_match_the_single_call():
+    banner("cascade staged calls")
+    from gpu_helpers import cascade_device, pa
+
+    wl, dw = named("qwen3_8b_radix")
+    whole = bits(gpu_cascade(wl, dw))
+    gs, ppt, shl, gmax, msh = cascade_device(wl)
+    T = torch()
+    out = T.empty_like(dw.q)
+    nb = pa().decode_cascade_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                             wl.max_seq_len, gs.numel() - 1, gmax, msh)
+    ws = T.empty(nb, dtype=T.uint8, device="cuda")
+    for stage in ("prefix", "suffix", "combine"):
+        pa().decode_cascade(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, gs, gmax, ppt,
+                            shl, msh, wl.scale, out=out, workspace=ws, stage=stage)
+    T.cuda.synchronize()
+    assert bits(out) == whole

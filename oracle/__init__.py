@@ -14,3 +14,4 @@ from .paged_attention import (  # noqa: F401
     token_slots,
     widen,
 )
+from .rope import rope, rope_kv_store  # noqa: F401

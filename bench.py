@@ -129,6 +129,41 @@ def copy_calibration(iters=10):
     return 2 * nread / (ms * 1e-3) / 1e9, nread, ms
 
 
+def bench_rope(pa, W, torch, np, stream, iters):
+    """pa_rope_kv_store on the chunked-prefill workload's 4096 new rows:
+    rotate q (32 heads) and k (8 heads), store k and v.  HBM-bound."""
+    ew = W.make("qwen3_8b_extend")
+    edw = W.to_device(ew)
+    pos = ew.positions()
+    cos_t, sin_t = W.rope_tables(int(ew.max_seq_len), ew.head_dim)
+    pos_d = torch.from_numpy(pos).cuda()
+    cos_d, sin_d = torch.from_numpy(cos_t).cuda(), torch.from_numpy(sin_t).cuda()
+    q_out = torch.empty_like(edw.q)
+
+    def f():
+        pa.rope_kv_store(edw.k_pool, edw.v_pool, edw.q, edw.k_new, edw.v_new, pos_d, edw.slot_mapping, cos_d, sin_d,
+                         q_out=q_out)
+
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(iters):
+        f()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    N, Hq, Hkv, D, es = len(pos), ew.num_q_heads, ew.num_kv_heads, ew.head_dim, ew.elem_bytes
+    # q read + written, k and v read + written, distinct table rows, positions and slots
+    alg = 2 * N * Hq * D * es + 4 * N * Hkv * D * es + len(np.unique(pos)) * D * 4 + N * (4 + 8)
+    gbps = alg / (ms * 1e-3) / 1e9
+    return {"workload": "qwen3_8b_extend (4096 new rows)", "kernel_us": round(ms * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": int(alg)}}
+
+
 def cpu_baseline(wl, target_s):
     """The oracle, as it stands, on a bounded sample of the workload."""
     import numpy as np
@@ -389,6 +424,12 @@ def main():
                          "algorithmic_flops_per_launch": flops},
         }
         log(f"extend: {ems * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+
+    # ---------------- fused rotary embedding + store (the step before attention)
+    if not args.no_extend:
+        result["rope_kv_store"] = bench_rope(pa, W, torch, np, stream, max(5, args.steps // 2))
+        log(f"rope+store: {result['rope_kv_store']['kernel_us']} us, "
+            f"{result['rope_kv_store']['roofline']['achieved']} GB/s")
 
     # ---------------- plain-copy reference on the same device
     cgb, _, _ = copy_calibration()

@@ -10,6 +10,11 @@
  *   pa_kv_store    write a step's new K/V rows into the pool slots given by a
  *                  slot mapping ("mini-sglang from Scratch", section "How this
  *                  book works": the KV-cache writes);
+ *   pa_rope_kv_store
+ *                  the same store fused with the rotary position embedding
+ *                  that precedes it: q and k rotated with half-split pairing
+ *                  (nanoSGLang README, section Notable Fixes), k and v
+ *                  written to the pool;
  *   pa_decode      one new token per request attends every cached key of its
  *                  request through the page table, grouped-query heads
  *                  (Mini-SGLang README, section Reference Attention Backends;
@@ -110,6 +115,37 @@ const char* pa_status_string(int32_t status);
  */
 pa_status pa_kv_store(const pa_kv_pool* pool, const void* k_new, const void* v_new,
                       const int64_t* slot_mapping, int64_t num_rows, void* stream);
+
+/*
+ * pa_rope_kv_store: pa_kv_store with the rotary position embedding of q and k
+ * done on the way.  For each row i in [0, num_rows) with slot_mapping[i] >= 0
+ * and p = positions[i]:
+ *   q_out[i, h, :] = rope(q[i, h, :], p)   for every query head h
+ *   k pool at flat slot slot_mapping[i] = rope(k_new[i], p)
+ *   v pool at that slot = v_new[i]          (byte copy)
+ * where rope turns each channel pair (j, j + head_dim/2) of a head by the
+ * angle whose cosine and sine are cos_table[p, j] and sin_table[p, j]:
+ *   (a, b) -> (a * cos - b * sin, b * cos + a * sin).
+ * Rows with a negative slot are padding: nothing is read or written for them
+ * (their q_out rows are left as they are).
+ *   q, q_out        [num_rows, num_q_heads, head_dim], pool dtype, 16-byte
+ *                   aligned; q_out may be q (in place).  num_q_heads may be
+ *                   0 (keys only; q and q_out are then not used).
+ *   k_new, v_new    [num_rows, num_kv_heads, head_dim], pool dtype, 16-byte
+ *                   aligned.
+ *   positions       int32 [num_rows]; values outside [0, max_position) are a
+ *                   contract violation and are clamped (no access leaves the
+ *                   tables).
+ *   cos_table, sin_table
+ *                   fp32 [max_position, head_dim / 2], row-major, 16-byte
+ *                   aligned (an engine's precomputed rotary cache).
+ * The arithmetic is fp32 with one rounding to the pool dtype at the end.
+ * Slots must be distinct; overlapping slots are undefined.
+ */
+pa_status pa_rope_kv_store(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const void* k_new,
+                           const void* v_new, const int32_t* positions, const int64_t* slot_mapping,
+                           int64_t num_rows, const float* cos_table, const float* sin_table, int32_t max_position,
+                           void* q_out, void* stream);
 
 /*
  * Decode split plan.  The key range of each request is cut into consecutive

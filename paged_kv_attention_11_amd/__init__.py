@@ -65,6 +65,7 @@ SIGNATURES = {
     "pa_version": (ctypes.c_char_p, []),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_kv_store": (_i32, [_POOLP, _vp, _vp, _vp, _i64, _vp]),
+    "pa_rope_kv_store": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp]),
     "pa_decode_split_tokens": (_i32, [_i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
@@ -172,6 +173,38 @@ def kv_store(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
     st = load().pa_kv_store(ctypes.byref(pool), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                             slot_mapping.numel(), _stream(stream))
     _check(st, "pa_kv_store")
+
+
+def rope_kv_store(k_pool, v_pool, q, k_new, v_new, positions, slot_mapping, cos_table, sin_table, q_out=None,
+                  stream=None):
+    """Rotate q [N, H_q, D] and k_new [N, H_kv, D] by the rotary tables
+    (fp32 [max_position, D/2]) at `positions` (int32 [N]); write the rotated
+    keys and v_new to slot_mapping's slots of the pools; return q_out."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, n, k_pool.dtype)
+    if q is not None:
+        _dev(q, "q", k_pool.dtype)
+    _dev(positions, "positions", torch.int32)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(cos_table, "cos_table", torch.float32)
+    _dev(sin_table, "sin_table", torch.float32)
+    N = slot_mapping.numel()
+    if positions.numel() != N or k_new.shape[0] != N or v_new.shape[0] != N or (q is not None and q.shape[0] != N):
+        raise ValueError("q, k_new, v_new, positions and slot_mapping must have the same number of rows")
+    if cos_table.dim() != 2 or cos_table.shape[1] * 2 != k_pool.shape[3] or sin_table.shape != cos_table.shape:
+        raise ValueError("cos_table and sin_table must be [max_position, head_dim / 2]")
+    Hq = 0 if q is None else q.shape[1]
+    if q is not None and q_out is None:
+        q_out = torch.empty_like(q)
+    if q_out is not None:
+        _dev(q_out, "q_out", k_pool.dtype)
+    st = load().pa_rope_kv_store(ctypes.byref(pool), _ptr(q), Hq, _ptr(k_new), _ptr(v_new), _ptr(positions),
+                                 _ptr(slot_mapping), N, _ptr(cos_table), _ptr(sin_table), cos_table.shape[0],
+                                 _ptr(q_out), _stream(stream))
+    _check(st, "pa_rope_kv_store")
+    return q_out
 
 
 def decode_split_tokens(num_seqs: int, num_kv_heads: int, max_seq_len: int) -> int:

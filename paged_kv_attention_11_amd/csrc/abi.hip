@@ -204,6 +204,41 @@ pa_status pa_kv_store(const pa_kv_pool* pool, const void* k_new, const void* v_n
   return hip_status(pa::launch_kv_store(a, (hipStream_t)stream));
 }
 
+pa_status pa_rope_kv_store(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const void* k_new,
+                           const void* v_new, const int32_t* positions, const int64_t* slot_mapping,
+                           int64_t num_rows, const float* cos_table, const float* sin_table, int32_t max_position,
+                           void* q_out, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_rows < 0 || num_q_heads < 0 || max_position <= 0) return PA_ERR_SHAPE;
+  if (num_rows == 0) return PA_OK;
+  if (!k_new || !v_new || !positions || !slot_mapping || !cos_table || !sin_table) return PA_ERR_NULL;
+  if (num_q_heads > 0 && (!q || !q_out)) return PA_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(cos_table, 16) || !aligned(sin_table, 16))
+    return PA_ERR_SHAPE;
+  if (num_q_heads > 0 && (!aligned(q, 16) || !aligned(q_out, 16))) return PA_ERR_SHAPE;
+  if (num_rows * (num_q_heads + 2 * (int64_t)pool->num_kv_heads) * pool->head_dim > ((int64_t)1 << 50))
+    return PA_ERR_SHAPE;
+  pa::RopeArgs a;
+  a.q = q;
+  a.q_out = q_out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.positions = positions;
+  a.slot_mapping = slot_mapping;
+  a.cos_table = cos_table;
+  a.sin_table = sin_table;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.num_rows = num_rows;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.max_position = max_position;
+  a.bf16 = pool->dtype == PA_BF16;
+  return hip_status(pa::launch_rope_store(a, (hipStream_t)stream));
+}
+
 int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
   return auto_split(num_seqs, num_kv_heads, max_seq_len);
 }

@@ -25,6 +25,25 @@ struct StoreArgs {
   int32_t row_chunks;  // bytes of one [num_kv_heads, head_dim] row / 16
 };
 
+struct RopeArgs {
+  const void* q;
+  void* q_out;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* positions;
+  const int64_t* slot_mapping;
+  const float* cos_table;  // [max_position, head_dim / 2]
+  const float* sin_table;
+  void* k_pool;
+  void* v_pool;
+  int64_t num_rows;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_position;
+  int32_t bf16;
+};
+
 struct GatherArgs {
   const void* k_pool;
   const void* v_pool;
@@ -97,6 +116,7 @@ struct ExtendArgs {
 
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_rope_store(const RopeArgs& a, hipStream_t stream);
 // Return hipErrorInvalidValue for an instantiation that does not exist
 // (the ABI layer validates first, so this is a guard, not a code path).
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);

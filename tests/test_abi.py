@@ -218,3 +218,20 @@ def test_binding_refuses_cpu_tensors():
     k = torch.zeros(4, 16, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pa.kv_store(k, k, k[0], k[0], torch.zeros(1, dtype=torch.int64))
+
+
+def rope(p, q=FAKE, Hq=32, k=FAKE, v=FAKE, pos=FAKE, slots=FAKE, n=4, cos=FAKE, sin=FAKE, maxp=4096, qo=FAKE):
+    return pa.load().pa_rope_kv_store(ctypes.byref(p), q, Hq, k, v, pos, slots, n, cos, sin, maxp, qo, None)
+
+
+def test_rope_store_validation():
+    p = pool()
+    assert rope(p, n=-1) == SHAPE
+    assert rope(p, maxp=0) == SHAPE
+    assert rope(p, Hq=-1) == SHAPE
+    assert rope(p, n=0) == OK
+    for kw in ("k", "v", "pos", "slots", "cos", "sin", "q", "qo"):
+        assert rope(p, **{kw: 0}) == NULL, kw
+    assert rope(p, cos=FAKE + 4) == SHAPE
+    assert rope(p, q=FAKE + 8) == SHAPE
+    assert rope(pool(dtype=5)) == DTYPE

@@ -129,6 +129,15 @@ class Workload:
             ppt[j, :len(self.shared_pages[j])] = self.shared_pages[j]
         return starts, ppt, (self.shared_counts.astype(np.int64) * P).astype(np.int32)
 
+    def positions(self) -> np.ndarray:
+        """int32 [N]: the position of each new row (new token i of request b
+        sits at seq_len_b - n_b + i), the index rotary tables are read at."""
+        out = np.empty(int(self.q_indptr[-1]) if self.num_seqs else 0, np.int32)
+        for b in range(self.num_seqs):
+            n, L = int(self.n_new[b]), int(self.seq_lens[b])
+            out[self.q_indptr[b]:self.q_indptr[b + 1]] = np.arange(L - n, L)
+        return out
+
     @property
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
@@ -418,6 +427,18 @@ def make_custom(seq_lens, num_q_heads, num_kv_heads, head_dim, page_size, dtype=
                  num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                  page_size=page_size, num_pages=num_pages, seed=seed, poison=poison,
                  radix=radix, stride=stride)
+
+
+def rope_tables(max_position: int, head_dim: int, theta: float = 1.0e6):
+    """The rotary cache an engine precomputes, as the inputs of the fused
+    rope + store call: cos and sin of p * theta^(-2j / head_dim) for
+    p < max_position, j < head_dim / 2, rounded to float32 (theta 1e6 is the
+    Qwen3 value).  Input data only: neither side of the parity tests derives
+    it."""
+    half = head_dim // 2
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -35,6 +35,14 @@
  *                  from Scratch", section "What you will be able to do"):
  *                  each shared page is read once per group of requests
  *                  instead of once per request;
+ *   pa_attend_mixed
+ *                  one call for the mixed batches continuous batching makes
+ *                  (nanoSGLang README, section Features: continuous batching
+ *                  with mixed prefill and decode): requests with one new
+ *                  token take the decode kernels, the others the extend
+ *                  kernel; fixed buffers padded with empty requests
+ *                  ("mini-sglang from Scratch": CUDA Graph's fixed-buffer
+ *                  contract) let a whole step be captured once and replayed;
  *   pa_gather      copy requests' pages out to contiguous K/V (test and
  *                  calibration helper: the legacy per-token copy that paged
  *                  attention removes, nanoSGLang README, section Ablation).
@@ -314,6 +322,28 @@ pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32
                                     const int32_t* shared_lens, int32_t max_shared_len, float scale,
                                     int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * pa_attend_mixed: the result of pa_extend (same q, q_indptr, page_table,
+ * seq_lens, out) for a batch that mixes decode requests (one new row) with
+ * chunked-prefill or verify chunks (several new rows).  Requests with exactly
+ * one new row go through the split-K decode kernels (their keys are split
+ * over many work-groups), the others through the matrix-core extend kernel;
+ * requests with no new row (q_indptr[b+1] == q_indptr[b], seq_len 0) are
+ * padding and produce nothing.  Enqueues three kernels: decode partial,
+ * extend (only if max_q_len > 1), combine.
+ *   split_tokens, workspace, workspace_bytes: as for pa_decode, sized by
+ *                   pa_decode_workspace_bytes(num_seqs, num_q_heads,
+ *                   num_kv_heads, head_dim, max_seq_len, split_tokens).
+ *   max_q_len, max_seq_len: host-side bounds; the grids and the split plan
+ *                   depend only on them, so a captured call can be replayed
+ *                   with other device-side contents within the same bounds.
+ * bf16 pools only, head_dim 128 or 64, group size 1, 2, 4 or 8.
+ */
+pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* q_indptr,
+                          const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t max_q_len, int32_t max_seq_len, float scale, int32_t split_tokens, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_gather: copy the first seq_lens[b] tokens of every request, in logical

@@ -114,6 +114,7 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   a.head_dim = pool->head_dim;
   a.log2_page = ilog2(pool->page_size);
   a.key_begin = nullptr;
+  a.q_indptr = nullptr;
   a.split_tokens = split;
   a.max_splits = (int32_t)S;
   a.piece_offset = 0;
@@ -478,6 +479,53 @@ pa_status pa_decode_cascade_combine(PA_CASCADE_PARAMS) { return cascade_impl(PA_
 
 #undef PA_CASCADE_PARAMS
 #undef PA_CASCADE_ARGS
+
+pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* q_indptr,
+                          const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t max_q_len, int32_t max_seq_len, float scale, int32_t split_tokens, void* out,
+                          void* workspace, size_t workspace_bytes_, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs, max_seq_len,
+                                scale, split_tokens, out, workspace, workspace_bytes_, a);
+  if (st != PA_OK) return st;
+  if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (max_q_len < 0 || max_q_len > max_seq_len) return PA_ERR_SHAPE;
+  const int64_t qblocks = (max_q_len + 128 / G - 1) / (128 / G);
+  if (qblocks * pool->num_kv_heads * num_seqs > (int64_t)INT_MAX) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!q_indptr) return PA_ERR_NULL;
+  if (!aligned(out, 16)) return PA_ERR_SHAPE;
+  a.q_indptr = q_indptr;
+  a.always_partial = 0;
+  const hipStream_t hs = (hipStream_t)stream;
+  // requests with one new row: split-K decode; the others: matrix-core tiles
+  st = hip_status(pa::launch_decode_partial(a, hs));
+  if (st != PA_OK) return st;
+  if (max_q_len > 1) {
+    pa::ExtendArgs e = {};
+    e.k_pool = pool->k_pool;
+    e.v_pool = pool->v_pool;
+    e.q = q;
+    e.q_indptr = q_indptr;
+    e.page_table = page_table;
+    e.seq_lens = seq_lens;
+    e.out = out;
+    e.pt_stride = pt_stride;
+    e.num_seqs = num_seqs;
+    e.num_q_heads = num_q_heads;
+    e.num_kv_heads = pool->num_kv_heads;
+    e.head_dim = pool->head_dim;
+    e.log2_page = ilog2(pool->page_size);
+    e.max_q_len = max_q_len;
+    e.skip_single = 1;
+    e.scale_log2 = scale * kLog2e;
+    st = hip_status(pa::launch_extend(e, hs));
+    if (st != PA_OK) return st;
+  }
+  return hip_status(pa::launch_decode_combine(a, hs));
+}
 
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
                     const int32_t* seq_lens, const int64_t* out_offsets, int32_t num_seqs,

@@ -143,6 +143,14 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   const int g = bg % p.num_kv_heads;
   const int b = bg / p.num_kv_heads;
 
+  // Mixed batch: only requests with one new row, whose query and output
+  // row is q_indptr[b].
+  int qrow = b;
+  if (p.q_indptr) {
+    qrow = p.q_indptr[b];
+    if (p.q_indptr[b + 1] - qrow != 1) return;  // uniform over the work-group
+  }
+
   // This request's key range is [k0, L); piece s covers split_tokens of it.
   const int L = p.seq_lens[b];
   const int k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   const int vr = lane / LPR;  // key row within a V load instruction
   const int vc = lane % LPR;  // 16-byte piece within the V row
   {
-    const uint4* qb = (const uint4*)((const T*)p.q + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D);
+    const uint4* qb = (const uint4*)((const T*)p.q + ((int64_t)qrow * p.num_q_heads + (int64_t)g * G) * D);
     for (int i = tid; i < G * C::CPR; i += kThreads) (&s_q[0][0])[i] = qb[i];
   }
 
@@ -318,7 +326,8 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   __syncthreads();
 
   // ---- merge the waves and write the piece
-  const int64_t row0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;
+  const int64_t row0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;     // workspace rows
+  const int64_t orow0 = (int64_t)qrow * p.num_q_heads + (int64_t)g * G;  // output rows
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
@@ -335,9 +344,9 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
     o = o / lsum;
     if (n_splits == 1 && !p.always_partial) {
       if constexpr (BF16)
-        ((uint16_t*)p.out)[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
+        ((uint16_t*)p.out)[(orow0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
       else
-        ((float*)p.out)[(row0 + h) * D + d] = o;
+        ((float*)p.out)[(orow0 + h) * D + d] = o;
     } else {
       const int64_t r = (row0 + h) * p.ws_pieces + p.piece_offset + s;
       p.o_part[r * D + d] = o;
@@ -362,6 +371,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p)
   const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
   if (row >= rows) return;
   const int b = (int)(row / p.num_q_heads);
+  int64_t orow = row;  // output row
+  if (p.q_indptr) {
+    const int r0 = p.q_indptr[b];
+    if (p.q_indptr[b + 1] - r0 != 1) return;  // not a decode request of a mixed batch
+    orow = (int64_t)r0 * p.num_q_heads + (row - (int64_t)b * p.num_q_heads);
+  }
   const int L = p.seq_lens[b];
   const int k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
   // both counts are clamped to the pieces the workspace row holds
@@ -426,11 +441,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p)
     }
   }
   if constexpr (BF16) {
-    uint16_t* out = (uint16_t*)p.out + row * D + lane * EPL;
+    uint16_t* out = (uint16_t*)p.out + orow * D + lane * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(res[e]);
   } else {
-    float* out = (float*)p.out + row * D + lane * EPL;
+    float* out = (float*)p.out + orow * D + lane * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) out[e] = res[e];
   }

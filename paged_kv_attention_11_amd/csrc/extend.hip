@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void mfma_attn_kernel(const ExtendArgs p)
     const int r0 = p.q_indptr[b];
     const int n = p.q_indptr[b + 1] - r0;
     const int i0 = qb * TOK;
-    if (i0 >= n) return;
+    if (i0 >= n || (n == 1 && p.skip_single)) return;
     const int prefix = p.seq_lens[b] - n;
     k_begin = 0;
     k_end = prefix + min(i0 + TOK, n);  // keys this block can see

@@ -66,6 +66,9 @@ struct DecodeArgs {
   const int32_t* page_table;
   const int32_t* seq_lens;
   const int32_t* key_begin;  // [B] first key of each request's range, or null (0)
+  // [B+1] mixed batches: request b's new rows start at q_indptr[b]; only
+  // requests with exactly one new row are handled here.  Null: row b.
+  const int32_t* q_indptr;
   float* o_part;  // [B, Hq, ws_pieces, D]
   float* lse;     // [B, Hq, ws_pieces], log2 domain
   void* out;      // [B, Hq, D]
@@ -111,6 +114,7 @@ struct ExtendArgs {
   int32_t piece_keys;          // prefix: keys per piece
   int32_t num_pieces;          // prefix: pieces per group
   int32_t ws_pieces;           // prefix: workspace row stride in pieces
+  int32_t skip_single;         // extend: leave requests with one new row to the decode kernels
   float scale_log2;
 };
 

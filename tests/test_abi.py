@@ -235,3 +235,26 @@ def test_rope_store_validation():
     assert rope(p, cos=FAKE + 4) == SHAPE
     assert rope(p, q=FAKE + 8) == SHAPE
     assert rope(pool(dtype=5)) == DTYPE
+
+
+def mixed(p, q=FAKE, Hq=32, qi=FAKE, pt=FAKE, stride=64, sl=FAKE, B=4, qmax=128, Lmax=1000, split=0, out=FAKE,
+          ws=FAKE, ws_bytes=1 << 40):
+    return pa.load().pa_attend_mixed(ctypes.byref(p), q, Hq, qi, pt, stride, sl, B, qmax, Lmax, 0.1, split, out, ws,
+                                     ws_bytes, None)
+
+
+def test_mixed_validation():
+    p = pool()
+    assert mixed(pool(dtype=0)) == DTYPE
+    assert mixed(p, Hq=24) == UNSUP  # group 3: no matrix-core tile
+    assert mixed(p, Hq=30) == SHAPE
+    assert mixed(p, qmax=2000) == SHAPE
+    assert mixed(p, qmax=-1) == SHAPE
+    assert mixed(p, stride=10) == SHAPE
+    assert mixed(p, split=100) == SHAPE
+    assert mixed(p, qi=0) == NULL
+    assert mixed(p, q=0) == NULL
+    assert mixed(p, ws=0) == WS
+    assert mixed(p, ws_bytes=1000) == WS
+    assert mixed(p, out=FAKE + 4) == SHAPE
+    assert mixed(p, B=0, q=0, qi=0, pt=0, sl=0, out=0, ws=0) == OK

@@ -26,6 +26,7 @@ def test_config_shapes(name):
         "qwen3_06b_p1": (64, 16, 8, 128, 1, "bf16"),
         "qwen3_8b_radix": (256, 32, 8, 128, 16, "bf16"),
         "qwen3_8b_extend": (8, 32, 8, 128, 16, "bf16"),
+        "qwen3_8b_mixed": (256, 32, 8, 128, 16, "bf16"),
     }[name]
     assert (wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype) == spec
     assert wl.page_table.shape[1] * wl.page_size >= wl.max_seq_len
@@ -38,6 +39,10 @@ def test_config_shapes(name):
         assert L.min() >= 256 and L.max() <= 2048 and wl.num_pages == 200_000
     elif name == "qwen3_8b_radix":
         assert L.min() >= 512 and L.max() <= 8192 and wl.num_pages == 65_536
+    elif name == "qwen3_8b_mixed":
+        assert np.all(wl.n_new[:8] == 512) and np.all(wl.n_new[8:] == 1)
+        assert (L[:8] - 512).min() >= 0 and (L[:8] - 512).max() <= 4096
+        assert L[8:].min() >= 512 and L[8:].max() <= 8192
     else:
         p = L - wl.n_new
         assert np.all(wl.n_new == 512) and p.min() >= 0 and p.max() <= 4096
@@ -50,7 +55,7 @@ def test_config_shapes(name):
         np.testing.assert_array_equal(wl.slot_mapping[wl.q_indptr[b]:wl.q_indptr[b + 1]], expect)
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen25_05b", "qwen3_06b_p1", "qwen3_8b_extend"])
+@pytest.mark.parametrize("name", ["tiny", "qwen25_05b", "qwen3_06b_p1", "qwen3_8b_extend", "qwen3_8b_mixed"])
 def test_private_pages_are_distinct(name):
     wl = W.make(name, with_values=False)
     allp = np.concatenate(wl.page_lists)
@@ -116,3 +121,16 @@ def test_values_do_not_depend_on_thread_count(monkeypatch):
     monkeypatch.setattr(W.os, "cpu_count", lambda: 1)
     b = W._normal_f32(5, 1, 3 * W._CHUNK + 17)
     assert a.tobytes() == b.tobytes()
+
+
+def test_positions_are_the_new_rows_absolute_positions():
+    wl = W.make_custom([10, 3, 7], 4, 2, 64, 4, dtype="bf16", kind="extend", n_new=[4, 1, 7], seed=1)
+    assert wl.positions().tolist() == [6, 7, 8, 9, 2, 0, 1, 2, 3, 4, 5, 6]
+
+
+def test_rope_tables_are_the_standard_schedule():
+    c, s = W.rope_tables(5, 8, theta=10000.0)
+    assert c.dtype == np.float32 and c.shape == (5, 4)
+    assert c[0].tolist() == [1.0] * 4 and s[0].tolist() == [0.0] * 4
+    # pair j turns by p * 10000^(-2j/8) at position p
+    assert abs(float(s[3, 1]) - math.sin(3 * 10000.0 ** (-0.25))) < 1e-7

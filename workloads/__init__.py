@@ -378,6 +378,17 @@ def _cfg_qwen3_8b_extend(rng):
                 stride=288)
 
 
+def _cfg_qwen3_8b_mixed(rng):
+    # a continuous-batching step: 8 chunked-prefill requests (the extend
+    # workload's shape) next to 248 decode requests (the decode workload's
+    # lengths, private pages)
+    p = rng.integers(0, 4097, size=8)
+    u = rng.uniform(math.log(512), math.log(8193), size=248)
+    L = np.concatenate([p + 512, np.floor(np.exp(u)).astype(np.int64)])
+    return dict(kind="extend", dtype="bf16", seq_lens=L, n_new=[512] * 8 + [1] * 248,
+                num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, num_pages=65_536, stride=512)
+
+
 CONFIGS: Dict[str, tuple] = {
     # name: (default seed, spec)
     "tiny": (1, _cfg_tiny),
@@ -385,6 +396,7 @@ CONFIGS: Dict[str, tuple] = {
     "qwen3_06b_p1": (3, _cfg_qwen3_06b_p1),
     "qwen3_8b_radix": (4, _cfg_qwen3_8b_radix),
     "qwen3_8b_extend": (5, _cfg_qwen3_8b_extend),
+    "qwen3_8b_mixed": (6, _cfg_qwen3_8b_mixed),
 }
 
 DESCRIPTIONS = {
@@ -395,6 +407,8 @@ DESCRIPTIONS = {
                       "groups of 16 share a 1024-token prefix, bf16",
     "qwen3_8b_extend": "Qwen3-8B-shaped chunked-prefill extend: 8 reqs, prefix U[0,4096] + 512-token chunk, "
                        "32/8 heads, D=128, page 16, bf16",
+    "qwen3_8b_mixed": "Qwen3-8B-shaped mixed step: 8 prefill chunks (prefix U[0,4096] + 512) and 248 decode reqs "
+                      "(L log-U[512,8192]), 32/8 heads, D=128, page 16, bf16",
 }
 
 

@@ -164,6 +164,68 @@ def bench_rope(pa, W, torch, np, stream, iters):
                          "algorithmic_bytes_per_launch": int(alg)}}
 
 
+def _time(torch, stream, f, iters):
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(iters):
+        f()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def bench_mixed(pa, W, torch, np, stream, iters):
+    """One continuous-batching step of the Qwen3-8B-shaped mixed workload
+    (8 prefill chunks of 512 rows + 248 decode requests): rope + store, then
+    the mixed attention call; launched eagerly and as one replayed HIP graph.
+    Also the attention alone routed (decode kernels for one-row requests)
+    against every request through the extend kernel."""
+    mw = W.make("qwen3_8b_mixed")
+    d = W.to_device(mw)
+    pos = torch.from_numpy(mw.positions()).cuda()
+    cos_t, sin_t = W.rope_tables(int(mw.max_seq_len), mw.head_dim)
+    cos_d, sin_d = torch.from_numpy(cos_t).cuda(), torch.from_numpy(sin_t).cuda()
+    q_rot, out = torch.empty_like(d.q), torch.empty_like(d.q)
+    nb = pa.decode_workspace_bytes(mw.num_seqs, mw.num_q_heads, mw.num_kv_heads, mw.head_dim, mw.max_seq_len)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def attend():
+        pa.attend_mixed(q_rot, d.q_indptr, d.k_pool, d.v_pool, d.page_table, d.seq_lens, mw.max_q_len, mw.max_seq_len,
+                        mw.scale, out=out, workspace=ws)
+
+    def step():
+        pa.rope_kv_store(d.k_pool, d.v_pool, d.q, d.k_new, d.v_new, pos, d.slot_mapping, cos_d, sin_d, q_out=q_rot)
+        attend()
+
+    def all_extend():
+        pa.extend(q_rot, d.q_indptr, d.k_pool, d.v_pool, d.page_table, d.seq_lens, mw.max_q_len, mw.max_seq_len,
+                  mw.scale, out=out)
+
+    eager = _time(torch, stream, step, iters)
+    routed = _time(torch, stream, attend, iters)
+    ext = _time(torch, stream, all_extend, iters)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    replay = _time(torch, stream, graph.replay, iters)
+    del graph
+    return {"workload": "qwen3_8b_mixed", "description": W.DESCRIPTIONS["qwen3_8b_mixed"],
+            "step": "rope_kv_store + attend_mixed", "eager_us": round(eager * 1e3, 1),
+            "graph_replay_us": round(replay * 1e3, 1), "attention_routed_us": round(routed * 1e3, 1),
+            "attention_all_extend_us": round(ext * 1e3, 1),
+            "tokens_per_s": round(int(mw.q_indptr[-1]) / (replay * 1e-3), 1)}
+
+
 def cpu_baseline(wl, target_s):
     """The oracle, as it stands, on a bounded sample of the workload."""
     import numpy as np
@@ -430,6 +492,13 @@ def main():
         result["rope_kv_store"] = bench_rope(pa, W, torch, np, stream, max(5, args.steps // 2))
         log(f"rope+store: {result['rope_kv_store']['kernel_us']} us, "
             f"{result['rope_kv_store']['roofline']['achieved']} GB/s")
+
+    # ---------------- a mixed continuous-batching step, eager and as a replayed graph
+    if not args.no_extend:
+        result["mixed_step"] = bench_mixed(pa, W, torch, np, stream, max(5, args.steps // 2))
+        m = result["mixed_step"]
+        log(f"mixed step: eager {m['eager_us']} us, graph {m['graph_replay_us']} us, "
+            f"all-extend attention {m['attention_all_extend_us']} us vs routed {m['attention_routed_us']} us")
 
     # ---------------- plain-copy reference on the same device
     cgb, _, _ = copy_calibration()

@@ -43,6 +43,11 @@
  *                  kernel; fixed buffers padded with empty requests
  *                  ("mini-sglang from Scratch": CUDA Graph's fixed-buffer
  *                  contract) let a whole step be captured once and replayed;
+ *   pa_verify      the same attention as pa_extend for short chunks: the
+ *                  parallel verification of k drafted tokens (Mini-SGLang
+ *                  README, section Speculative Decoding: one parallel
+ *                  prefill rather than k decodes), split over the keys like
+ *                  decode;
  *   pa_gather      copy requests' pages out to contiguous K/V (test and
  *                  calibration helper: the legacy per-token copy that paged
  *                  attention removes, nanoSGLang README, section Ablation).
@@ -322,6 +327,31 @@ pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32
                                     const int32_t* shared_lens, int32_t max_shared_len, float scale,
                                     int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * pa_verify: the result of pa_extend (same arguments and semantics) for
+ * requests whose chunks are short, as in the verification of drafted tokens:
+ * max_q_len * (num_q_heads / num_kv_heads) <= 32.  The keys of each request
+ * are split into pieces of split_tokens keys (0 = pa_decode_split_tokens'
+ * choice; else a multiple of 64 in [64, 1024]) handled by separate
+ * work-groups, each reading a K/V tile once for all rows of the chunk and all
+ * query heads of a KV head; a second kernel merges the pieces.
+ *   workspace: pa_verify_workspace_bytes(...) bytes, 256-byte aligned
+ *              (0 bytes and NULL allowed when one piece covers max_seq_len).
+ *              Layout: fp32 partial outputs [num_seqs, max_q_len,
+ *              num_q_heads, S, head_dim], then (256-byte aligned) fp32
+ *              log2-sum-exp [num_seqs, max_q_len, num_q_heads, S],
+ *              S = ceil(max_seq_len / split_tokens).
+ * Chunks longer than max_q_len are a contract violation (their extra rows
+ * are not computed).  bf16 pools only, head_dim 128 or 64, group size 1, 2,
+ * 4 or 8.  Softmax weights are rounded to bf16 before the weighted sum of V.
+ */
+size_t pa_verify_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t split_tokens);
+pa_status pa_verify(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* q_indptr,
+                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t max_q_len, int32_t max_seq_len, float scale, int32_t split_tokens, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_attend_mixed: the result of pa_extend (same q, q_indptr, page_table,

@@ -80,6 +80,8 @@ SIGNATURES = {
     "pa_decode_cascade_combine": (_i32, _CASCADE_ARGS),
     "pa_attend_mixed": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz,
                                _vp]),
+    "pa_verify_workspace_bytes": (_sz, [_i32] * 7),
+    "pa_verify": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
     "pa_gather": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
 }
 
@@ -377,6 +379,43 @@ def attend_mixed(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, m
                                 float(scale), int(split_tokens), _ptr(out), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "pa_attend_mixed")
+    return out
+
+
+def verify_workspace_bytes(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                           split_tokens=0) -> int:
+    return load().pa_verify_workspace_bytes(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                            split_tokens)
+
+
+def verify(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, max_seq_len, scale, out=None,
+           workspace=None, split_tokens=0, stream=None):
+    """Short-chunk extend (verification of drafted tokens): q [T_q, H_q, D]
+    bf16 -> out [T_q, H_q, D]; same result as extend(...)."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(q, "q", torch.bfloat16)
+    _dev(q_indptr, "q_indptr", torch.int32)
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != k_pool.shape[3]:
+        raise ValueError("q must be [T_q, num_q_heads, head_dim]")
+    B = seq_lens.numel()
+    if q_indptr.numel() != B + 1 or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("q_indptr [B+1], page_table [B, stride], seq_lens [B] must agree")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if workspace is None:
+        nbytes = verify_workspace_bytes(B, max_q_len, q.shape[1], k_pool.shape[2], k_pool.shape[3], max_seq_len,
+                                        split_tokens)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    st = load().pa_verify(ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(q_indptr), _ptr(page_table),
+                          page_table.shape[1], _ptr(seq_lens), B, int(max_q_len), int(max_seq_len), float(scale),
+                          int(split_tokens), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream(stream))
+    _check(st, "pa_verify")
     return out
 
 

@@ -527,6 +527,66 @@ pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_h
   return hip_status(pa::launch_decode_combine(a, hs));
 }
 
+size_t pa_verify_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t split_tokens) {
+  if (num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
+    return 0;
+  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
+  if (split < 0) return 0;
+  const int64_t S = (max_seq_len + split - 1) / split;
+  const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * (S > 1 ? S : 0);
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+pa_status pa_verify(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* q_indptr,
+                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t max_q_len, int32_t max_seq_len, float scale, int32_t split_tokens, void* out,
+                    void* workspace, size_t workspace_bytes_, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || max_q_len < 0 || max_seq_len < 0 || pt_stride < 0 || num_q_heads <= 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_q_len * G > 32) return PA_ERR_UNSUPPORTED;  // rows of one matrix-core tile pair
+  if (max_q_len > max_seq_len) return PA_ERR_SHAPE;
+  if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
+  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
+  if (split < 0) return PA_ERR_SHAPE;
+  const int64_t S = (max_seq_len + split - 1) / split;
+  if ((int64_t)num_seqs * pool->num_kv_heads * S > (int64_t)INT_MAX) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_q_len == 0 || max_seq_len == 0) return PA_OK;
+  if (!q || !q_indptr || !page_table || !seq_lens || !out) return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return PA_ERR_SHAPE;
+  const size_t need = pa_verify_workspace_bytes(num_seqs, max_q_len, num_q_heads, pool->num_kv_heads,
+                                                pool->head_dim, max_seq_len, split);
+  if (S > 1 && (workspace_bytes_ < need || !workspace || !aligned(workspace, 256))) return PA_ERR_WORKSPACE;
+  const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * (S > 1 ? S : 0);
+  pa::VerifyArgs a = {};
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.q = q;
+  a.q_indptr = q_indptr;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.o_part = S > 1 ? (float*)workspace : nullptr;
+  a.lse = S > 1 ? (float*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float))) : nullptr;
+  a.pt_stride = pt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.log2_page = ilog2(pool->page_size);
+  a.max_q_len = max_q_len;
+  a.split_tokens = split;
+  a.max_splits = (int32_t)S;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(pa::launch_verify(a, (hipStream_t)stream));
+}
+
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
                     const int32_t* seq_lens, const int64_t* out_offsets, int32_t num_seqs,
                     int32_t max_seq_len, void* k_out, void* v_out, void* stream) {

@@ -118,6 +118,30 @@ struct ExtendArgs {
   float scale_log2;
 };
 
+// Short chunks (parallel verification of drafted tokens): split-K over keys,
+// the chunk's rows x G heads packed into 16x16 matrix-core tiles.
+struct VerifyArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;               // [T_q, H_q, D] bf16
+  const int32_t* q_indptr;     // [B+1]
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* out;                   // [T_q, H_q, D] bf16
+  float* o_part;               // [B, max_q_len, H_q, max_splits, D]
+  float* lse;                  // [B, max_q_len, H_q, max_splits]
+  int64_t pt_stride;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t log2_page;
+  int32_t max_q_len;           // rows per request; max_q_len * G <= 32
+  int32_t split_tokens;        // keys per piece, multiple of 64, <= 1024
+  int32_t max_splits;
+  float scale_log2;
+};
+
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_rope_store(const RopeArgs& a, hipStream_t stream);
@@ -127,5 +151,6 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const ExtendArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -1,0 +1,391 @@
+// Parallel verification of drafted tokens: every request brings a short
+// chunk of n new rows (k drafted tokens + 1, a handful) that attends its whole
+// cached context causally.  The target model verifies the k tokens in one
+// parallel prefill rather than k decodes (Mini-SGLang README, yangyonggit
+// fork, section Speculative Decoding), so the rows of a request are few and
+// its keys many: the work is shaped like decode, not like prefill.
+//
+// Design:
+//  * Split-K like decode: work-group = (piece s of split_tokens keys,
+//    request b, KV head g), piece index slowest; the pieces are merged by
+//    verify_combine_kernel with log-sum-exp weights.
+//  * The n rows x G query heads of (b, g) (at most 32) are packed into the
+//    N dimension of 16x16 matrix-core tiles, two halves of 16 rows, so each
+//    K/V byte is read once for all of them.
+//  * K and V tiles of 64 keys come from the pages straight into a 3-deep LDS
+//    ring (the extend kernel's pipeline); the four waves split every tile by
+//    keys, 16 each: S^T = K Q^T with v_mfma_f32_16x16x32_bf16, then
+//    O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand (keys x
+//    rows) is exactly the score accumulator's layout, so P never leaves
+//    registers; V^T is read with the transposing LDS read.
+//  * Each wave keeps its own running maximum, sum and O^T for all rows; the
+//    four waves are merged through LDS at the end of the piece.
+//  * Row (token i, head h) sees keys <= L - n + i; only the tiles that reach
+//    past L - n are masked.
+#include "device.h"
+#include "internal.h"
+#include "mfma_tile.h"
+
+namespace pa {
+
+namespace {
+
+using namespace tile;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = kTileThreads;
+constexpr int kVRows = 32;  // query rows of a work-group: two halves of 16
+constexpr float kSlack = 8.0f;  // log2 units: rescale only when the maximum grows by more
+
+__device__ __forceinline__ f32x4_t mfma16_k32(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16_k16(const uint2& a, const uint2& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                   c, 0, 0, 0);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
+  using C = ExtCfg<D>;
+  constexpr int PPR = C::PPR, NDMA = C::NDMA;
+  constexpr int KS = D / 32;  // 32-wide head-dim steps of S^T
+  constexpr int DC = D / 16;  // 16-wide head-dim chunks of O^T
+  constexpr int RS = D + 4;   // row stride (floats) of the merge buffer
+
+  // K ring, then V ring, in one array so the merge can reuse all of it
+  __shared__ uint4 s_ring[2][kStages][kKT * PPR];
+  __shared__ int32_t s_pages[kPageCap];
+  auto s_k = s_ring[0];
+  auto s_v = s_ring[1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+
+  // work-group -> (piece s, request b, KV head g), piece index slowest
+  const int units = p.num_seqs * p.num_kv_heads;
+  const int s = blockIdx.x / units;
+  const int u = blockIdx.x - s * units;
+  const int g = u % p.num_kv_heads;
+  const int b = u / p.num_kv_heads;
+  const int r0 = p.q_indptr[b];
+  const int n = p.q_indptr[b + 1] - r0;
+  const int L = p.seq_lens[b];
+  const int k_begin = s * p.split_tokens;
+  if (n <= 0 || k_begin >= L) return;  // uniform over the work-group
+  const int k_end = min(k_begin + p.split_tokens, L);
+  const int prefix = L - n;
+  const int nq = min(n, p.max_q_len);  // rows computed (more than max_q_len breaks the contract)
+  const int ns = (L + p.split_tokens - 1) / p.split_tokens;
+  const int ntiles = (k_end - k_begin + kKT - 1) / kKT;
+
+  // ---- queries: row = i * G + h; this lane supplies row 16 rh + l16 of the
+  // B operand, head dims 32 ks + 8 grp .. + 7
+  uint4 qreg[2][KS];
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) {
+    const int row = rh * 16 + l16;
+    const int i = row / G, h = row % G;
+    const bool ok = i < nq;
+    const uint16_t* qp =
+        (const uint16_t*)p.q + ((int64_t)(r0 + (ok ? i : 0)) * p.num_q_heads + (int64_t)g * G + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[rh][ks] = ok ? *(const uint4*)(qp + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
+  }
+  // retire the query loads once, so the key loop carries no wait for them
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t v = __builtin_bit_cast(u32x4_t, qreg[rh][ks]);
+      asm volatile("" : "+v"(v));
+      qreg[rh][ks] = __builtin_bit_cast(uint4, v);
+    }
+
+  // ---- page ids of the piece (split_tokens <= 1024 keys: at most 1024 pages)
+  const int sh = p.log2_page;
+  const int pmask = (1 << sh) - 1;
+  const int pg0 = k_begin >> sh;
+  const int npg = ((k_end - 1) >> sh) - pg0 + 1;
+  {
+    const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride + pg0;
+    for (int i = tid; i < npg; i += kThreads) s_pages[i] = pt[i];
+  }
+  __syncthreads();
+
+  const int64_t row_stride = (int64_t)p.num_kv_heads * D;
+  const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)g * D;
+  const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)g * D;
+
+  // DMA of tile t into ring slot sb; keys past the piece are clamped to its
+  // last key (a real row, masked out of the softmax)
+  auto issue_tile = [&](int t, int sb) {
+    const int pc = lane % PPR;
+#pragma unroll
+    for (int m = 0; m < NDMA; ++m) {
+      const int blk = wave * NDMA + m;
+      const int key = blk * C::RPB + lane / PPR;
+      const int kk = min(k_begin + t * kKT + key, k_end - 1);
+      const int32_t page = s_pages[(kk >> sh) - pg0];
+      const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride;
+      dma16(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(key)) * 8);
+      dma16(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(key)) * 8);
+    }
+  };
+
+  f32x4_t o[DC][2];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) o[dc][rh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {-INFINITY, -INFINITY};  // raw-score reference maximum per row
+  float l_run[2] = {0.f, 0.f};              // this lane's part of the row sums
+  const float sl2 = p.scale_log2;
+  const float slack = kSlack / sl2;
+
+  // ---- prologue: tiles 0 and 1 in flight
+  issue_tile(0, 0);
+  if (ntiles > 1) {
+    issue_tile(1, 1);
+    vm_wait<2 * NDMA>();
+  } else {
+    vm_wait<0>();
+  }
+  __syncthreads();
+
+  const int key_l = 16 * wave + l16;  // key row this lane supplies to the K operand
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t % kStages;
+    const bool ahead = (t + 2) < ntiles;
+    if (ahead) issue_tile(t + 2, (t + 2) % kStages);
+
+    // ---- S^T for this wave's 16 keys: lane holds keys 4 grp + r, row 16 rh + l16
+    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 a = s_k[buf][key_l * PPR + ((4 * ks + grp) ^ k_swz<D>(key_l))];
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) sacc[rh] = mfma16_k32(a, qreg[rh][ks], sacc[rh]);
+    }
+
+    // ---- causal mask and the keys past the piece, on the last tiles only
+    const int kt0 = k_begin + t * kKT;
+    if (kt0 + kKT - 1 > prefix || kt0 + kKT > k_end) {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const int i = (rh * 16 + l16) / G;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt0 + 16 * wave + 4 * grp + r;
+          if (key > prefix + i || key >= k_end) sacc[rh][r] = -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax: row maximum over this lane's 4 keys and the lanes
+    // holding the same row (lane ^ 16, lane ^ 32)
+    float mx[2];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+      float v = fmaxf(fmaxf(sacc[rh][0], sacc[rh][1]), fmaxf(sacc[rh][2], sacc[rh][3]));
+      v = fmaxf(v, shfl_xor_f(v, 16));
+      mx[rh] = fmaxf(v, shfl_xor_f(v, 32));
+    }
+    if (__ballot(mx[0] > m_ref[0] + slack || mx[1] > m_ref[1] + slack) != 0) {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const float m_new = fmaxf(m_ref[rh], mx[rh]);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref[rh] - m_new) * sl2);
+        m_ref[rh] = m_new;
+        l_run[rh] *= alpha;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) o[dc][rh] *= alpha;
+      }
+    }
+    uint2 pb[2];  // P^T B operands: keys 4 grp .. + 3 of row 16 rh + l16
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+      const float mb = m_ref[rh] == -INFINITY ? 0.f : -m_ref[rh] * sl2;
+      float e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e[r] = fast_exp2(fmaf(sacc[rh][r], sl2, mb));
+        l_run[rh] += e[r];
+      }
+      pb[rh] = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
+    }
+
+    // ---- O^T += V^T P^T: lane (grp, j) addresses key 16 wave + 4 grp + j/4,
+    // head dims 16 dc + 4 (j % 4) .. + 3, and receives V[4 keys][16 dc + j]
+    {
+      const char* vb = (const char*)&s_v[buf][0];
+      const int kr = 16 * wave + 4 * grp + (l16 >> 2);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const int d = 16 * dc + 4 * (l16 & 3);
+        const int lp = d >> 3;
+        const int within = (d & 4) ? 8 : 0;
+        const uint2 x = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) o[dc][rh] = mfma16_k16(x, pb[rh], o[dc][rh]);
+      }
+    }
+
+    if (ahead) vm_wait<2 * NDMA>(); else vm_wait<0>();
+    __syncthreads();
+  }
+
+  // ---- merge the four waves through LDS (the ring is free now)
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) {
+    l_run[rh] += shfl_xor_f(l_run[rh], 16);
+    l_run[rh] += shfl_xor_f(l_run[rh], 32);
+  }
+  float* red_m = (float*)&s_ring[0][0][0];       // [4][32]
+  float* red_l = red_m + kDecodeWaves * kVRows;   // [4][32]
+  float* red_o = red_l + kDecodeWaves * kVRows;   // [4][32][RS]
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) {
+    const int row = rh * 16 + l16;
+    if (grp == 0) {
+      red_m[wave * kVRows + row] = m_ref[rh];
+      red_l[wave * kVRows + row] = l_run[rh];
+    }
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      *(float4*)&red_o[(wave * kVRows + row) * RS + 16 * dc + 4 * grp] =
+          make_float4(o[dc][rh][0], o[dc][rh][1], o[dc][rh][2], o[dc][rh][3]);
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < kVRows * D; idx += kThreads) {
+    const int row = idx / D;
+    const int d = idx - row * D;
+    const int i = row / G, h = row % G;
+    if (i >= nq) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, red_m[w * kVRows + row]);
+    float ov = 0.f, lse = -INFINITY;
+    if (M != -INFINITY) {
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float mw = red_m[w * kVRows + row];
+        const float f = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * sl2);
+        lsum = fmaf(f, red_l[w * kVRows + row], lsum);
+        ov = fmaf(f, red_o[(w * kVRows + row) * RS + d], ov);
+      }
+      ov = ov / lsum;
+      lse = M * sl2 + __log2f(lsum);
+    }
+    const int64_t head = (int64_t)g * G + h;
+    if (ns == 1) {
+      ((uint16_t*)p.out)[((int64_t)(r0 + i) * p.num_q_heads + head) * D + d] = (uint16_t)f32_to_bf16_bits(ov);
+    } else {
+      const int64_t wr = (((int64_t)b * p.max_q_len + i) * p.num_q_heads + head) * p.max_splits + s;
+      p.o_part[wr * D + d] = ov;
+      if (d == 0) p.lse[wr] = lse;  // -inf: no key of this piece is visible to the row
+    }
+  }
+}
+
+// One wave per (request b, row i < max_q_len, query head): merge the pieces
+// of rows whose request has more than one piece; pieces the row cannot see
+// carry lse = -inf and get weight zero.
+template <int D>
+__global__ __launch_bounds__(256) void verify_combine_kernel(const VerifyArgs p) {
+  constexpr int EPL = D / 64;
+  constexpr int BATCH = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads;
+  if (R >= rows) return;
+  const int hq = (int)(R % p.num_q_heads);
+  const int64_t bi = R / p.num_q_heads;
+  const int i = (int)(bi % p.max_q_len);
+  const int b = (int)(bi / p.max_q_len);
+  const int r0 = p.q_indptr[b];
+  if (i >= p.q_indptr[b + 1] - r0) return;
+  const int L = p.seq_lens[b];
+  const int ns = min((L + p.split_tokens - 1) / p.split_tokens, p.max_splits);
+  if (ns <= 1) return;  // written by the partial kernel
+  const float* lse = p.lse + R * p.max_splits;
+  const float* op = p.o_part + R * p.max_splits * D + lane * EPL;
+
+  float M = -INFINITY;
+  for (int c = 0; c < ns; c += 64) M = fmaxf(M, lse[min(c + lane, ns - 1)]);
+  M = wave_max(M);
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int c = 0; c < ns; c += 64) {
+      const float l = lse[min(c + lane, ns - 1)];
+      const float w = (c + lane < ns && l != -INFINITY) ? fast_exp2(l - M) : 0.f;
+      wsum += w;
+      const int cnt = min(64, ns - c);
+      for (int j0 = 0; j0 < cnt; j0 += BATCH) {
+        float wk[BATCH], v[BATCH][EPL];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const int j = min(j0 + k, cnt - 1);
+          wk[k] = j0 + k < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
+                               : 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[k][e] = op[(int64_t)(c + j) * D + e];
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = wk[k] > 0.f ? fmaf(wk[k], v[k][e], o[e]) : o[e];
+      }
+    }
+    wsum = wave_sum(wsum);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] /= wsum;
+  }
+  uint16_t* out = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + hq) * D + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(o[e]);
+}
+
+template <int D, int G>
+hipError_t launch_g(const VerifyArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.num_seqs * a.num_kv_heads * a.max_splits;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((verify_kernel<D, G>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_splits <= 1) return e;
+  const int64_t rows = (int64_t)a.num_seqs * a.max_q_len * a.num_q_heads;
+  hipLaunchKernelGGL((verify_combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const VerifyArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_g<D, 1>(a, stream);
+    case 2: return launch_g<D, 2>(a, stream);
+    case 4: return launch_g<D, 4>(a, stream);
+    case 8: return launch_g<D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -258,3 +258,36 @@ def test_mixed_validation():
     assert mixed(p, ws_bytes=1000) == WS
     assert mixed(p, out=FAKE + 4) == SHAPE
     assert mixed(p, B=0, q=0, qi=0, pt=0, sl=0, out=0, ws=0) == OK
+
+
+def verify(p, q=FAKE, Hq=32, qi=FAKE, pt=FAKE, stride=64, sl=FAKE, B=4, qmax=6, Lmax=1000, split=0, out=FAKE,
+           ws=FAKE, ws_bytes=1 << 40):
+    return pa.load().pa_verify(ctypes.byref(p), q, Hq, qi, pt, stride, sl, B, qmax, Lmax, 0.1, split, out, ws,
+                               ws_bytes, None)
+
+
+def test_verify_validation():
+    p = pool()
+    assert verify(pool(dtype=0)) == DTYPE
+    assert verify(p, Hq=24) == UNSUP
+    assert verify(p, qmax=9) == UNSUP  # 9 rows x 4 heads > 32
+    assert verify(p, Hq=64, qmax=5) == UNSUP  # 5 x 8 > 32
+    assert verify(p, Hq=30) == SHAPE
+    assert verify(p, qmax=-1) == SHAPE
+    assert verify(p, stride=10) == SHAPE
+    assert verify(p, split=100) == SHAPE
+    assert verify(p, q=0) == NULL
+    assert verify(p, qi=0) == NULL
+    assert verify(p, out=FAKE + 4) == SHAPE
+    assert verify(p, ws=0) == WS
+    assert verify(p, ws_bytes=4096) == WS
+    assert verify(p, B=0) == OK and verify(p, qmax=0) == OK
+
+
+def test_verify_workspace_size():
+    lib = pa.load()
+    # 64 requests x 6 rows x 32 heads, split 1024 over 8192 keys: 8 pieces
+    rows = 64 * 6 * 32 * 8
+    expect = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 8192, 1024) == expect
+    assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 1000, 1024) == 0  # one piece: no workspace

@@ -1,0 +1,79 @@
+"""Short-chunk extend (parallel verification of drafted tokens) against the
+oracle's extend, which pins it (a verify chunk is an extend chunk; the
+oracle's extend row i equals its decode at length p + i + 1)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_close, bits, f64, fresh, gpu_extend, pa, stored_oracle_pools, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def gpu_verify(wl, dw, split=0, max_q_len=None):
+    o = pa().verify(dw.q, dw.q_indptr, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens,
+                    max_q_len or wl.max_q_len, wl.max_seq_len, wl.scale, split_tokens=split)
+    torch().cuda.synchronize()
+    return o
+
+
+VERIFY_SWEEP = [
+    # (prefixes, rows per request, Hq, Hkv, D, P, split)
+    ([500, 3000, 0, 63, 64, 1000], [6, 6, 6, 6, 6, 6], 32, 8, 128, 16, 0),
+    ([500, 3000, 0, 63, 64, 1000], [6, 6, 6, 6, 6, 6], 32, 8, 128, 16, 64),   # many pieces, masks in the last
+    ([2000, 10], [8, 8], 32, 8, 128, 16, 1024),                                 # 8 x 4 = 32 rows
+    ([700, 0, 129], [1, 3, 6], 32, 8, 128, 16, 128),                            # uneven chunks, one decode row
+    ([900, 33], [4, 4], 64, 8, 128, 16, 0),                                     # group 8
+    ([900, 33], [16, 2], 16, 8, 128, 1, 256),                                   # group 2, page 1
+    ([300, 4100], [32, 5], 4, 4, 128, 64, 192),                                 # group 1, 32 rows
+    ([1500, 70], [6, 6], 8, 2, 64, 16, 0),                                      # D = 64
+    ([0, 0], [1, 2], 8, 2, 128, 16, 0),                                         # tiny contexts
+]
+
+
+@pytest.mark.parametrize("case", range(len(VERIFY_SWEEP)))
+def test_verify_sweep(case):
+    prefixes, n, Hq, Hkv, D, P, split = VERIFY_SWEEP[case]
+    banner(f"verify sweep {case}: prefixes={prefixes} n={n} Hq={Hq} Hkv={Hkv} D={D} P={P} split={split}")
+    lens = [p + k for p, k in zip(prefixes, n)]
+    wl = W.make_custom(lens, Hq, Hkv, D, P, dtype="bf16", kind="extend", n_new=n, seed=700 + case)
+    dw = fresh(wl)
+    out = f64(gpu_verify(wl, dw, split))
+    kp, vp = stored_oracle_pools(wl)
+    ref = oracle.extend(wl.q, wl.q_indptr, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    assert_close(out, ref, f"verify sweep {case}")
+    assert_close(out, f64(gpu_extend(wl, dw)), f"verify sweep {case} vs extend")
+
+
+def test_verify_padding_requests_and_bound_above_the_chunks():
+    """Requests with no rows (and no keys) are skipped; max_q_len may exceed
+    every chunk."""
+    banner("verify padding")
+    wl = W.make_custom([600, 0, 80, 0], 32, 8, 128, 16, dtype="bf16", kind="extend", n_new=[6, 0, 3, 0], seed=720)
+    dw = fresh(wl)
+    out = f64(gpu_verify(wl, dw, 64, max_q_len=8))
+    kp, vp = stored_oracle_pools(wl)
+    ref = oracle.extend(wl.q, wl.q_indptr, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    assert_close(out, ref, "verify padding")
+
+
+def test_verify_qwen3_8b_workload_sampled_and_deterministic():
+    banner("verify qwen3_8b_verify")
+    wl = W.make("qwen3_8b_verify")
+    dw = fresh(wl)
+    first = gpu_verify(wl, dw)
+    assert bits(gpu_verify(wl, dw)) == bits(first)
+    out = f64(first)
+    kp, vp = stored_oracle_pools(wl)
+    order = np.argsort(wl.seq_lens)
+    seqs = sorted(set(order[:3].tolist()) | set(order[-3:].tolist()) | set(range(0, 64, 9)))
+    sub = wl.subset(seqs)
+    ref = oracle.extend(sub.q, sub.q_indptr, kp, vp, sub.page_table, sub.seq_lens, wl.scale, wl.dtype)
+    rows = np.concatenate([np.arange(wl.q_indptr[b], wl.q_indptr[b + 1]) for b in seqs])
+    err = assert_close(out[rows], ref, "qwen3_8b_verify")
+    print(f"[result] verify: {len(seqs)} requests checked, max abs err {err:.3g}", flush=True)

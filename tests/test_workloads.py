@@ -27,6 +27,7 @@ def test_config_shapes(name):
         "qwen3_8b_radix": (256, 32, 8, 128, 16, "bf16"),
         "qwen3_8b_extend": (8, 32, 8, 128, 16, "bf16"),
         "qwen3_8b_mixed": (256, 32, 8, 128, 16, "bf16"),
+        "qwen3_8b_verify": (64, 32, 8, 128, 16, "bf16"),
     }[name]
     assert (wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype) == spec
     assert wl.page_table.shape[1] * wl.page_size >= wl.max_seq_len
@@ -39,6 +40,8 @@ def test_config_shapes(name):
         assert L.min() >= 256 and L.max() <= 2048 and wl.num_pages == 200_000
     elif name == "qwen3_8b_radix":
         assert L.min() >= 512 and L.max() <= 8192 and wl.num_pages == 65_536
+    elif name == "qwen3_8b_verify":
+        assert np.all(wl.n_new == 6) and L.min() >= 512 + 6 - 1 and L.max() <= 8192
     elif name == "qwen3_8b_mixed":
         assert np.all(wl.n_new[:8] == 512) and np.all(wl.n_new[8:] == 1)
         assert (L[:8] - 512).min() >= 0 and (L[:8] - 512).max() <= 4096
@@ -55,7 +58,8 @@ def test_config_shapes(name):
         np.testing.assert_array_equal(wl.slot_mapping[wl.q_indptr[b]:wl.q_indptr[b + 1]], expect)
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen25_05b", "qwen3_06b_p1", "qwen3_8b_extend", "qwen3_8b_mixed"])
+@pytest.mark.parametrize("name", ["tiny", "qwen25_05b", "qwen3_06b_p1", "qwen3_8b_extend", "qwen3_8b_mixed",
+                                  "qwen3_8b_verify"])
 def test_private_pages_are_distinct(name):
     wl = W.make(name, with_values=False)
     allp = np.concatenate(wl.page_lists)

@@ -389,6 +389,15 @@ def _cfg_qwen3_8b_mixed(rng):
                 num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, num_pages=65_536, stride=512)
 
 
+def _cfg_qwen3_8b_verify(rng):
+    # speculative verification: k = 5 drafted tokens + 1 checked in one pass
+    # per request, after a context of the decode workload's lengths
+    u = rng.uniform(math.log(512), math.log(8193 - 6), size=64)
+    L = np.floor(np.exp(u)).astype(np.int64) + 6
+    return dict(kind="extend", dtype="bf16", seq_lens=L, n_new=[6] * 64,
+                num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, num_pages=16_384, stride=512)
+
+
 CONFIGS: Dict[str, tuple] = {
     # name: (default seed, spec)
     "tiny": (1, _cfg_tiny),
@@ -397,6 +406,7 @@ CONFIGS: Dict[str, tuple] = {
     "qwen3_8b_radix": (4, _cfg_qwen3_8b_radix),
     "qwen3_8b_extend": (5, _cfg_qwen3_8b_extend),
     "qwen3_8b_mixed": (6, _cfg_qwen3_8b_mixed),
+    "qwen3_8b_verify": (7, _cfg_qwen3_8b_verify),
 }
 
 DESCRIPTIONS = {
@@ -409,6 +419,8 @@ DESCRIPTIONS = {
                        "32/8 heads, D=128, page 16, bf16",
     "qwen3_8b_mixed": "Qwen3-8B-shaped mixed step: 8 prefill chunks (prefix U[0,4096] + 512) and 248 decode reqs "
                       "(L log-U[512,8192]), 32/8 heads, D=128, page 16, bf16",
+    "qwen3_8b_verify": "Qwen3-8B-shaped speculative verify: 64 reqs, 6 new rows (k=5 drafts + 1) after a context "
+                       "log-U[512,8187], 32/8 heads, D=128, page 16, bf16",
 }
 
 

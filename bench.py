@@ -177,6 +177,43 @@ def _time(torch, stream, f, iters):
     return s.elapsed_time(e) / iters
 
 
+def bench_verify(pa, W, torch, np, stream, iters):
+    """pa_verify on the Qwen3-8B-shaped verify workload (64 requests, 6 new
+    rows each after contexts of 512..8192 keys), against pa_extend on the same
+    batch.  HBM-bound: each request's K/V is read once for its 6 x 4 query
+    rows per KV head."""
+    vw = W.make("qwen3_8b_verify")
+    d = W.to_device(vw)
+    pa.kv_store(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slot_mapping)
+    out = torch.empty_like(d.q)
+    nb = pa.verify_workspace_bytes(vw.num_seqs, vw.max_q_len, vw.num_q_heads, vw.num_kv_heads, vw.head_dim,
+                                   vw.max_seq_len)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+
+    def ver():
+        pa.verify(d.q, d.q_indptr, d.k_pool, d.v_pool, d.page_table, d.seq_lens, vw.max_q_len, vw.max_seq_len,
+                  vw.scale, out=out, workspace=ws)
+
+    def ext():
+        pa.extend(d.q, d.q_indptr, d.k_pool, d.v_pool, d.page_table, d.seq_lens, vw.max_q_len, vw.max_seq_len,
+                  vw.scale, out=out)
+
+    ms = _time(torch, stream, ver, iters)
+    ems = _time(torch, stream, ext, iters)
+    kv = vw.kv_bytes_unique()
+    P = vw.page_size
+    alg = kv + 2 * int(vw.q_indptr[-1]) * vw.num_q_heads * vw.head_dim * 2 + \
+        4 * int(sum((int(L) + P - 1) // P for L in vw.seq_lens))
+    gbps = alg / (ms * 1e-3) / 1e9
+    return {"workload": "qwen3_8b_verify", "description": W.DESCRIPTIONS["qwen3_8b_verify"],
+            "kernel_us": round(ms * 1e3, 2), "extend_us": round(ems * 1e3, 2),
+            "rows_per_s": round(int(vw.q_indptr[-1]) / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": int(alg),
+                         "note": "verify kernel + its combine; K/V counted once per request"}}
+
+
 def bench_mixed(pa, W, torch, np, stream, iters):
     """One continuous-batching step of the Qwen3-8B-shaped mixed workload
     (8 prefill chunks of 512 rows + 248 decode requests): rope + store, then
@@ -492,6 +529,12 @@ def main():
         result["rope_kv_store"] = bench_rope(pa, W, torch, np, stream, max(5, args.steps // 2))
         log(f"rope+store: {result['rope_kv_store']['kernel_us']} us, "
             f"{result['rope_kv_store']['roofline']['achieved']} GB/s")
+
+    # ---------------- short-chunk verify (speculative decoding)
+    if not args.no_extend:
+        result["verify"] = bench_verify(pa, W, torch, np, stream, max(5, args.steps // 2))
+        v = result["verify"]
+        log(f"verify: {v['kernel_us']} us ({v['roofline']['achieved']} GB/s) vs extend {v['extend_us']} us")
 
     # ---------------- a mixed continuous-batching step, eager and as a replayed graph
     if not args.no_extend:

@@ -12,14 +12,15 @@
 //  * The n rows x G query heads of (b, g) (at most 32) are packed into the
 //    N dimension of 16x16 matrix-core tiles, two halves of 16 rows, so each
 //    K/V byte is read once for all of them.
-//  * K and V tiles of 64 keys come from the pages straight into a 3-deep LDS
-//    ring (the extend kernel's pipeline); the four waves split every tile by
-//    keys, 16 each: S^T = K Q^T with v_mfma_f32_16x16x32_bf16, then
+//  * K and V tiles of 64 keys come from the pages straight into an LDS ring
+//    (the extend kernel's pipeline).  Every wave computes the scores of
+//    the whole tile, S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (cheap next
+//    to the memory time), and a quarter of the output head dims,
 //    O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand (keys x
 //    rows) is exactly the score accumulator's layout, so P never leaves
 //    registers; V^T is read with the transposing LDS read.
-//  * Each wave keeps its own running maximum, sum and O^T for all rows; the
-//    four waves are merged through LDS at the end of the piece.
+//  * The waves therefore hold identical running maxima and sums and disjoint
+//    output columns: nothing is merged between them at the end of a piece.
 //  * Row (token i, head h) sees keys <= L - n + i; only the tiles that reach
 //    past L - n are masked.
 #include "device.h"
@@ -35,7 +36,6 @@ using namespace tile;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = kTileThreads;
-constexpr int kVRows = 32;  // query rows of a work-group: two halves of 16
 constexpr float kSlack = 8.0f;  // log2 units: rescale only when the maximum grows by more
 
 __device__ __forceinline__ f32x4_t mfma16_k32(const uint4& a, const uint4& b, const f32x4_t& c) {
@@ -47,19 +47,37 @@ __device__ __forceinline__ f32x4_t mfma16_k16(const uint2& a, const uint2& b, co
                                                    c, 0, 0, 0);
 }
 
+// LDS ring depth: kVStages - 1 tiles in flight per work-group.  Two stages
+// (64 KB for D = 128) let two work-groups share a compute unit, which hides
+// more latency than a third stage in one work-group (190 vs 237 us on the
+// Qwen3-8B-shaped verify workload).
+#ifndef PA_VERIFY_STAGES
+#define PA_VERIFY_STAGES 2
+#endif
+constexpr int kVStages = PA_VERIFY_STAGES;
+
+// Wait until tile t + 1 has landed while the tiles issued after it (at most
+// kVStages - 2, fewer near the end) stay in flight.
+template <int NDMA>
+__device__ __forceinline__ void wait_next(int after) {
+  if constexpr (kVStages >= 4) {
+    if (after >= 2) { vm_wait<4 * NDMA>(); return; }
+  }
+  if (after >= 1) vm_wait<2 * NDMA>(); else vm_wait<0>();
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   using C = ExtCfg<D>;
   constexpr int PPR = C::PPR, NDMA = C::NDMA;
-  constexpr int KS = D / 32;  // 32-wide head-dim steps of S^T
-  constexpr int DC = D / 16;  // 16-wide head-dim chunks of O^T
-  constexpr int RS = D + 4;   // row stride (floats) of the merge buffer
+  constexpr int KS = D / 32;           // 32-wide head-dim steps of S^T
+  constexpr int DCW = D / 16 / 4;      // 16-wide output chunks per wave
+  constexpr int NJ = kKT / 16;         // 16-key slices of a tile
+  static_assert(DCW >= 1, "head_dim too small");
 
-  // K ring, then V ring, in one array so the merge can reuse all of it
-  __shared__ uint4 s_ring[2][kStages][kKT * PPR];
+  __shared__ uint4 s_k[kVStages][kKT * PPR];
+  __shared__ uint4 s_v[kVStages][kKT * PPR];
   __shared__ int32_t s_pages[kPageCap];
-  auto s_k = s_ring[0];
-  auto s_v = s_ring[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,39 +157,38 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
     }
   };
 
-  f32x4_t o[DC][2];
+  f32x4_t o[DCW][2];  // O^T chunk dc = wave * DCW + c: lane holds d = 16 dc + 4 grp + r, row 16 rh + l16
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc)
+  for (int c = 0; c < DCW; ++c)
 #pragma unroll
-    for (int rh = 0; rh < 2; ++rh) o[dc][rh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rh = 0; rh < 2; ++rh) o[c][rh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref[2] = {-INFINITY, -INFINITY};  // raw-score reference maximum per row
   float l_run[2] = {0.f, 0.f};              // this lane's part of the row sums
   const float sl2 = p.scale_log2;
   const float slack = kSlack / sl2;
 
-  // ---- prologue: tiles 0 and 1 in flight
-  issue_tile(0, 0);
-  if (ntiles > 1) {
-    issue_tile(1, 1);
-    vm_wait<2 * NDMA>();
-  } else {
-    vm_wait<0>();
-  }
+  // ---- prologue: tiles 0 .. kVStages - 2 in flight, tile 0 landed
+  for (int t = 0; t < kVStages - 1 && t < ntiles; ++t) issue_tile(t, t);
+  wait_next<NDMA>(min(kVStages - 2, ntiles - 1));
   __syncthreads();
 
-  const int key_l = 16 * wave + l16;  // key row this lane supplies to the K operand
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t % kStages;
-    const bool ahead = (t + 2) < ntiles;
-    if (ahead) issue_tile(t + 2, (t + 2) % kStages);
+    const int buf = t % kVStages;
+    if (t + kVStages - 1 < ntiles) issue_tile(t + kVStages - 1, (t + kVStages - 1) % kVStages);
 
-    // ---- S^T for this wave's 16 keys: lane holds keys 4 grp + r, row 16 rh + l16
-    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    // ---- S^T of the whole tile: slice j, lane holds keys 16 j + 4 grp + r, row 16 rh + l16
+    f32x4_t sacc[NJ][2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 a = s_k[buf][key_l * PPR + ((4 * ks + grp) ^ k_swz<D>(key_l))];
+    for (int j = 0; j < NJ; ++j) {
+      sacc[j][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sacc[j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int key_l = 16 * j + l16;
 #pragma unroll
-      for (int rh = 0; rh < 2; ++rh) sacc[rh] = mfma16_k32(a, qreg[rh][ks], sacc[rh]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 a = s_k[buf][key_l * PPR + ((4 * ks + grp) ^ k_swz<D>(key_l))];
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) sacc[j][rh] = mfma16_k32(a, qreg[rh][ks], sacc[j][rh]);
+      }
     }
 
     // ---- causal mask and the keys past the piece, on the last tiles only
@@ -181,19 +198,24 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
       for (int rh = 0; rh < 2; ++rh) {
         const int i = (rh * 16 + l16) / G;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt0 + 16 * wave + 4 * grp + r;
-          if (key > prefix + i || key >= k_end) sacc[rh][r] = -INFINITY;
-        }
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kt0 + 16 * j + 4 * grp + r;
+            if (key > prefix + i || key >= k_end) sacc[j][rh][r] = -INFINITY;
+          }
       }
     }
 
-    // ---- online softmax: row maximum over this lane's 4 keys and the lanes
+    // ---- online softmax: row maximum over this lane's keys and the lanes
     // holding the same row (lane ^ 16, lane ^ 32)
     float mx[2];
 #pragma unroll
     for (int rh = 0; rh < 2; ++rh) {
-      float v = fmaxf(fmaxf(sacc[rh][0], sacc[rh][1]), fmaxf(sacc[rh][2], sacc[rh][3]));
+      float v = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        v = fmaxf(v, fmaxf(fmaxf(sacc[j][rh][0], sacc[j][rh][1]), fmaxf(sacc[j][rh][2], sacc[j][rh][3])));
       v = fmaxf(v, shfl_xor_f(v, 16));
       mx[rh] = fmaxf(v, shfl_xor_f(v, 32));
     }
@@ -205,93 +227,79 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
         m_ref[rh] = m_new;
         l_run[rh] *= alpha;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) o[dc][rh] *= alpha;
+        for (int c = 0; c < DCW; ++c) o[c][rh] *= alpha;
       }
     }
-    uint2 pb[2];  // P^T B operands: keys 4 grp .. + 3 of row 16 rh + l16
+    uint2 pb[NJ][2];  // P^T B operands: keys 16 j + 4 grp .. + 3 of row 16 rh + l16
 #pragma unroll
     for (int rh = 0; rh < 2; ++rh) {
       const float mb = m_ref[rh] == -INFINITY ? 0.f : -m_ref[rh] * sl2;
-      float e[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        e[r] = fast_exp2(fmaf(sacc[rh][r], sl2, mb));
-        l_run[rh] += e[r];
+      for (int j = 0; j < NJ; ++j) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = fast_exp2(fmaf(sacc[j][rh][r], sl2, mb));
+          l_run[rh] += e[r];
+        }
+        pb[j][rh] = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
       }
-      pb[rh] = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
     }
 
-    // ---- O^T += V^T P^T: lane (grp, j) addresses key 16 wave + 4 grp + j/4,
-    // head dims 16 dc + 4 (j % 4) .. + 3, and receives V[4 keys][16 dc + j]
+    // ---- O^T += V^T P^T for this wave's head dims: lane (grp, l16) addresses
+    // key 16 j + 4 grp + l16/4, dims 16 dc + 4 (l16 % 4) .. + 3, and receives
+    // V[4 keys][16 dc + l16]
     {
       const char* vb = (const char*)&s_v[buf][0];
-      const int kr = 16 * wave + 4 * grp + (l16 >> 2);
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const int d = 16 * dc + 4 * (l16 & 3);
+      for (int c = 0; c < DCW; ++c) {
+        const int d = 16 * (wave * DCW + c) + 4 * (l16 & 3);
         const int lp = d >> 3;
         const int within = (d & 4) ? 8 : 0;
-        const uint2 x = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
 #pragma unroll
-        for (int rh = 0; rh < 2; ++rh) o[dc][rh] = mfma16_k16(x, pb[rh], o[dc][rh]);
+        for (int j = 0; j < NJ; ++j) {
+          const int kr = 16 * j + 4 * grp + (l16 >> 2);
+          const uint2 x = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) o[c][rh] = mfma16_k16(x, pb[j][rh], o[c][rh]);
+        }
       }
     }
 
-    if (ahead) vm_wait<2 * NDMA>(); else vm_wait<0>();
+    // tiles issued after t + 1: min(kVStages - 2, ntiles - 2 - t)
+    wait_next<NDMA>(min(kVStages - 2, ntiles - 2 - t));
     __syncthreads();
   }
 
-  // ---- merge the four waves through LDS (the ring is free now)
+  // ---- write this wave's columns of every valid row
 #pragma unroll
   for (int rh = 0; rh < 2; ++rh) {
     l_run[rh] += shfl_xor_f(l_run[rh], 16);
     l_run[rh] += shfl_xor_f(l_run[rh], 32);
-  }
-  float* red_m = (float*)&s_ring[0][0][0];       // [4][32]
-  float* red_l = red_m + kDecodeWaves * kVRows;   // [4][32]
-  float* red_o = red_l + kDecodeWaves * kVRows;   // [4][32][RS]
-#pragma unroll
-  for (int rh = 0; rh < 2; ++rh) {
     const int row = rh * 16 + l16;
-    if (grp == 0) {
-      red_m[wave * kVRows + row] = m_ref[rh];
-      red_l[wave * kVRows + row] = l_run[rh];
-    }
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      *(float4*)&red_o[(wave * kVRows + row) * RS + 16 * dc + 4 * grp] =
-          make_float4(o[dc][rh][0], o[dc][rh][1], o[dc][rh][2], o[dc][rh][3]);
-  }
-  __syncthreads();
-
-  for (int idx = tid; idx < kVRows * D; idx += kThreads) {
-    const int row = idx / D;
-    const int d = idx - row * D;
     const int i = row / G, h = row % G;
     if (i >= nq) continue;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, red_m[w * kVRows + row]);
-    float ov = 0.f, lse = -INFINITY;
-    if (M != -INFINITY) {
-      float lsum = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float mw = red_m[w * kVRows + row];
-        const float f = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * sl2);
-        lsum = fmaf(f, red_l[w * kVRows + row], lsum);
-        ov = fmaf(f, red_o[(w * kVRows + row) * RS + d], ov);
-      }
-      ov = ov / lsum;
-      lse = M * sl2 + __log2f(lsum);
-    }
+    const bool seen = m_ref[rh] != -INFINITY;  // false: no key of this piece is visible to the row
+    const float inv = seen ? 1.f / l_run[rh] : 0.f;
     const int64_t head = (int64_t)g * G + h;
     if (ns == 1) {
-      ((uint16_t*)p.out)[((int64_t)(r0 + i) * p.num_q_heads + head) * D + d] = (uint16_t)f32_to_bf16_bits(ov);
+      uint16_t* op = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + head) * D;
+#pragma unroll
+      for (int c = 0; c < DCW; ++c) {
+        const int d = 16 * (wave * DCW + c) + 4 * grp;
+        *(uint2*)(op + d) = make_uint2(pack_bf16x2(o[c][rh][0] * inv, o[c][rh][1] * inv),
+                                       pack_bf16x2(o[c][rh][2] * inv, o[c][rh][3] * inv));
+      }
     } else {
       const int64_t wr = (((int64_t)b * p.max_q_len + i) * p.num_q_heads + head) * p.max_splits + s;
-      p.o_part[wr * D + d] = ov;
-      if (d == 0) p.lse[wr] = lse;  // -inf: no key of this piece is visible to the row
+      float* op = p.o_part + wr * D;
+#pragma unroll
+      for (int c = 0; c < DCW; ++c) {
+        const int d = 16 * (wave * DCW + c) + 4 * grp;
+        *(float4*)(op + d) = make_float4(o[c][rh][0] * inv, o[c][rh][1] * inv, o[c][rh][2] * inv,
+                                         o[c][rh][3] * inv);
+      }
+      if (wave == 0 && grp == 0) p.lse[wr] = seen ? m_ref[rh] * sl2 + __log2f(l_run[rh]) : -INFINITY;
     }
   }
 }

@@ -13,14 +13,14 @@
 //    N dimension of 16x16 matrix-core tiles, two halves of 16 rows, so each
 //    K/V byte is read once for all of them.
 //  * K and V tiles of 64 keys come from the pages straight into an LDS ring
-//    (the extend kernel's pipeline).  Every wave computes the scores of
-//    the whole tile, S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (cheap next
-//    to the memory time), and a quarter of the output head dims,
+//    (the extend kernel's pipeline).  Wave w takes row half w % 2 and head-dim
+//    half w / 2: it computes the scores of its 16 rows over the whole tile,
+//    S^T = K Q^T with v_mfma_f32_16x16x32_bf16, and its half of their output,
 //    O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand (keys x
 //    rows) is exactly the score accumulator's layout, so P never leaves
 //    registers; V^T is read with the transposing LDS read.
-//  * The waves therefore hold identical running maxima and sums and disjoint
-//    output columns: nothing is merged between them at the end of a piece.
+//  * The two waves of a row half hold identical running maxima and sums and
+//    disjoint output columns: nothing is merged between waves at the end.
 //  * Row (token i, head h) sees keys <= L - n + i; only the tiles that reach
 //    past L - n are masked.
 #include "device.h"
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   using C = ExtCfg<D>;
   constexpr int PPR = C::PPR, NDMA = C::NDMA;
   constexpr int KS = D / 32;           // 32-wide head-dim steps of S^T
-  constexpr int DCW = D / 16 / 4;      // 16-wide output chunks per wave
+  constexpr int DCW = D / 16 / 2;      // 16-wide output chunks per wave (half the head dims)
   constexpr int NJ = kKT / 16;         // 16-key slices of a tile
   static_assert(DCW >= 1, "head_dim too small");
 
@@ -84,6 +84,8 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
+  const int rh = wave & 1;   // row half: rows 16 rh .. 16 rh + 15
+  const int dg = wave >> 1;  // head-dim half of the output
 
   // work-group -> (piece s, request b, KV head g), piece index slowest
   const int units = p.num_seqs * p.num_kv_heads;
@@ -104,9 +106,8 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
 
   // ---- queries: row = i * G + h; this lane supplies row 16 rh + l16 of the
   // B operand, head dims 32 ks + 8 grp .. + 7
-  uint4 qreg[2][KS];
-#pragma unroll
-  for (int rh = 0; rh < 2; ++rh) {
+  uint4 qreg[KS];
+  {
     const int row = rh * 16 + l16;
     const int i = row / G, h = row % G;
     const bool ok = i < nq;
@@ -114,17 +115,15 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
         (const uint16_t*)p.q + ((int64_t)(r0 + (ok ? i : 0)) * p.num_q_heads + (int64_t)g * G + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qreg[rh][ks] = ok ? *(const uint4*)(qp + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
+      qreg[ks] = ok ? *(const uint4*)(qp + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
   }
   // retire the query loads once, so the key loop carries no wait for them
 #pragma unroll
-  for (int rh = 0; rh < 2; ++rh)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t v = __builtin_bit_cast(u32x4_t, qreg[rh][ks]);
-      asm volatile("" : "+v"(v));
-      qreg[rh][ks] = __builtin_bit_cast(uint4, v);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4_t v = __builtin_bit_cast(u32x4_t, qreg[ks]);
+    asm volatile("" : "+v"(v));
+    qreg[ks] = __builtin_bit_cast(uint4, v);
+  }
 
   // ---- page ids of the piece (split_tokens <= 1024 keys: at most 1024 pages)
   const int sh = p.log2_page;
@@ -157,13 +156,11 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
     }
   };
 
-  f32x4_t o[DCW][2];  // O^T chunk dc = wave * DCW + c: lane holds d = 16 dc + 4 grp + r, row 16 rh + l16
+  f32x4_t o[DCW];  // O^T chunk dc = dg * DCW + c: lane holds d = 16 dc + 4 grp + r, row 16 rh + l16
 #pragma unroll
-  for (int c = 0; c < DCW; ++c)
-#pragma unroll
-    for (int rh = 0; rh < 2; ++rh) o[c][rh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-INFINITY, -INFINITY};  // raw-score reference maximum per row
-  float l_run[2] = {0.f, 0.f};              // this lane's part of the row sums
+  for (int c = 0; c < DCW; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;  // raw-score reference maximum of this lane's row
+  float l_run = 0.f;        // this lane's part of the row sum
   const float sl2 = p.scale_log2;
   const float slack = kSlack / sl2;
 
@@ -176,73 +173,61 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
     const int buf = t % kVStages;
     if (t + kVStages - 1 < ntiles) issue_tile(t + kVStages - 1, (t + kVStages - 1) % kVStages);
 
-    // ---- S^T of the whole tile: slice j, lane holds keys 16 j + 4 grp + r, row 16 rh + l16
-    f32x4_t sacc[NJ][2];
+    // ---- S^T of the whole tile for this row half: slice j, lane holds keys
+    // 16 j + 4 grp + r of row 16 rh + l16
+    f32x4_t sacc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      sacc[j][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      sacc[j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int key_l = 16 * j + l16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint4 a = s_k[buf][key_l * PPR + ((4 * ks + grp) ^ k_swz<D>(key_l))];
-#pragma unroll
-        for (int rh = 0; rh < 2; ++rh) sacc[j][rh] = mfma16_k32(a, qreg[rh][ks], sacc[j][rh]);
+        sacc[j] = mfma16_k32(a, qreg[ks], sacc[j]);
       }
     }
 
     // ---- causal mask and the keys past the piece, on the last tiles only
     const int kt0 = k_begin + t * kKT;
     if (kt0 + kKT - 1 > prefix || kt0 + kKT > k_end) {
+      const int i = (rh * 16 + l16) / G;
 #pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {
-        const int i = (rh * 16 + l16) / G;
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kt0 + 16 * j + 4 * grp + r;
-            if (key > prefix + i || key >= k_end) sacc[j][rh][r] = -INFINITY;
-          }
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt0 + 16 * j + 4 * grp + r;
+          if (key > prefix + i || key >= k_end) sacc[j][r] = -INFINITY;
+        }
     }
 
     // ---- online softmax: row maximum over this lane's keys and the lanes
     // holding the same row (lane ^ 16, lane ^ 32)
-    float mx[2];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int rh = 0; rh < 2; ++rh) {
-      float v = -INFINITY;
+    for (int j = 0; j < NJ; ++j)
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[j][0], sacc[j][1]), fmaxf(sacc[j][2], sacc[j][3])));
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    if (__ballot(mx > m_ref + slack) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        v = fmaxf(v, fmaxf(fmaxf(sacc[j][rh][0], sacc[j][rh][1]), fmaxf(sacc[j][rh][2], sacc[j][rh][3])));
-      v = fmaxf(v, shfl_xor_f(v, 16));
-      mx[rh] = fmaxf(v, shfl_xor_f(v, 32));
+      for (int c = 0; c < DCW; ++c) o[c] *= alpha;
     }
-    if (__ballot(mx[0] > m_ref[0] + slack || mx[1] > m_ref[1] + slack) != 0) {
-#pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {
-        const float m_new = fmaxf(m_ref[rh], mx[rh]);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref[rh] - m_new) * sl2);
-        m_ref[rh] = m_new;
-        l_run[rh] *= alpha;
-#pragma unroll
-        for (int c = 0; c < DCW; ++c) o[c][rh] *= alpha;
-      }
-    }
-    uint2 pb[NJ][2];  // P^T B operands: keys 16 j + 4 grp .. + 3 of row 16 rh + l16
-#pragma unroll
-    for (int rh = 0; rh < 2; ++rh) {
-      const float mb = m_ref[rh] == -INFINITY ? 0.f : -m_ref[rh] * sl2;
+    uint2 pb[NJ];  // P^T B operands: keys 16 j + 4 grp .. + 3 of row 16 rh + l16
+    {
+      const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         float e[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          e[r] = fast_exp2(fmaf(sacc[j][rh][r], sl2, mb));
-          l_run[rh] += e[r];
+          e[r] = fast_exp2(fmaf(sacc[j][r], sl2, mb));
+          l_run += e[r];
         }
-        pb[j][rh] = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
+        pb[j] = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
       }
     }
 
@@ -253,15 +238,14 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
       const char* vb = (const char*)&s_v[buf][0];
 #pragma unroll
       for (int c = 0; c < DCW; ++c) {
-        const int d = 16 * (wave * DCW + c) + 4 * (l16 & 3);
+        const int d = 16 * (dg * DCW + c) + 4 * (l16 & 3);
         const int lp = d >> 3;
         const int within = (d & 4) ? 8 : 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int kr = 16 * j + 4 * grp + (l16 >> 2);
           const uint2 x = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
-#pragma unroll
-          for (int rh = 0; rh < 2; ++rh) o[c][rh] = mfma16_k16(x, pb[j][rh], o[c][rh]);
+          o[c] = mfma16_k16(x, pb[j], o[c]);
         }
       }
     }
@@ -271,36 +255,32 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
     __syncthreads();
   }
 
-  // ---- write this wave's columns of every valid row
+  // ---- write this wave's columns of its valid rows
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  const int row = rh * 16 + l16;
+  const int i = row / G, h = row % G;
+  if (i >= nq) return;
+  const bool seen = m_ref != -INFINITY;  // false: no key of this piece is visible to the row
+  const float inv = seen ? 1.f / l_run : 0.f;
+  const int64_t head = (int64_t)g * G + h;
+  if (ns == 1) {
+    uint16_t* op = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + head) * D;
 #pragma unroll
-  for (int rh = 0; rh < 2; ++rh) {
-    l_run[rh] += shfl_xor_f(l_run[rh], 16);
-    l_run[rh] += shfl_xor_f(l_run[rh], 32);
-    const int row = rh * 16 + l16;
-    const int i = row / G, h = row % G;
-    if (i >= nq) continue;
-    const bool seen = m_ref[rh] != -INFINITY;  // false: no key of this piece is visible to the row
-    const float inv = seen ? 1.f / l_run[rh] : 0.f;
-    const int64_t head = (int64_t)g * G + h;
-    if (ns == 1) {
-      uint16_t* op = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + head) * D;
-#pragma unroll
-      for (int c = 0; c < DCW; ++c) {
-        const int d = 16 * (wave * DCW + c) + 4 * grp;
-        *(uint2*)(op + d) = make_uint2(pack_bf16x2(o[c][rh][0] * inv, o[c][rh][1] * inv),
-                                       pack_bf16x2(o[c][rh][2] * inv, o[c][rh][3] * inv));
-      }
-    } else {
-      const int64_t wr = (((int64_t)b * p.max_q_len + i) * p.num_q_heads + head) * p.max_splits + s;
-      float* op = p.o_part + wr * D;
-#pragma unroll
-      for (int c = 0; c < DCW; ++c) {
-        const int d = 16 * (wave * DCW + c) + 4 * grp;
-        *(float4*)(op + d) = make_float4(o[c][rh][0] * inv, o[c][rh][1] * inv, o[c][rh][2] * inv,
-                                         o[c][rh][3] * inv);
-      }
-      if (wave == 0 && grp == 0) p.lse[wr] = seen ? m_ref[rh] * sl2 + __log2f(l_run[rh]) : -INFINITY;
+    for (int c = 0; c < DCW; ++c) {
+      const int d = 16 * (dg * DCW + c) + 4 * grp;
+      *(uint2*)(op + d) = make_uint2(pack_bf16x2(o[c][0] * inv, o[c][1] * inv),
+                                     pack_bf16x2(o[c][2] * inv, o[c][3] * inv));
     }
+  } else {
+    const int64_t wr = (((int64_t)b * p.max_q_len + i) * p.num_q_heads + head) * p.max_splits + s;
+    float* op = p.o_part + wr * D;
+#pragma unroll
+    for (int c = 0; c < DCW; ++c) {
+      const int d = 16 * (dg * DCW + c) + 4 * grp;
+      *(float4*)(op + d) = make_float4(o[c][0] * inv, o[c][1] * inv, o[c][2] * inv, o[c][3] * inv);
+    }
+    if (dg == 0 && grp == 0) p.lse[wr] = seen ? m_ref * sl2 + __log2f(l_run) : -INFINITY;
   }
 }
 

@@ -127,12 +127,11 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   return PA_OK;
 }
 
-// Shared-prefix pass of the cascade decode: keys per piece.  A work-group of
-// the matrix-core kernel holds a 96 KB LDS ring, so one runs per compute unit
-// and a tile costs about the same however many work-groups wait: the plan
-// aims at one work-group per compute unit, each looping over its piece's
-// tiles, rather than many short work-groups that each pay the prologue and
-// write partials.
+// Shared-prefix pass of the cascade decode: keys per piece.  The plan aims
+// at about 256 work-groups of the matrix-core kernel, each looping over the
+// tiles of its piece, rather than many short work-groups that each pay the
+// prologue and write partials (on the Qwen3-8B-shaped radix workload: 512-key
+// pieces 28 us, 256-key 27 us, 128-key 38 us, 64-key 72 us).
 constexpr int kPrefixTile = 64;   // keys per tile of the matrix-core kernel
 constexpr int kPrefixRows = 128;  // query rows per work-group of that kernel
 constexpr int64_t kPrefixTargetUnits = 256;

@@ -26,8 +26,9 @@
 //    also accumulated transposed, O^T += V^T P^T, so the rescale factor of a
 //    query row is lane-local and P goes from the score accumulator to the
 //    B operand without leaving registers.
-//  * K and V tiles (64 keys) are copied straight from the pages into a
-//    3-deep LDS ring with direct-to-LDS loads two tiles ahead; V stays in row
+//  * K and V tiles (64 keys) are copied straight from the pages into an LDS
+//    ring with direct-to-LDS loads one tile ahead, two work-groups per
+//    compute unit (registers cut to 2 waves per SIMD); V stays in row
 //    layout and is read into the A operand with transposing LDS reads.
 //  * Key tiles entirely above the diagonal are never visited; only tiles that
 //    cross it (or a row's key limit) are masked.
@@ -46,6 +47,20 @@ using namespace tile;
 constexpr int kThreads = kTileThreads;
 constexpr int kRows = 128;  // query rows per work-group
 
+// LDS ring depth and the waves per SIMD the register budget is cut for.  A
+// 2-stage ring (64 KB for D = 128) with registers cut to 256 lets two
+// work-groups share a compute unit, so one's softmax and LDS traffic overlap
+// the other's matrix-core work: 324 -> 260 us on the Qwen3-8B-shaped
+// chunked-prefill workload, where a deeper ring in one work-group per CU
+// changed nothing.
+#ifndef PA_EXTEND_STAGES
+#define PA_EXTEND_STAGES 2
+#endif
+#ifndef PA_EXTEND_WAVES
+#define PA_EXTEND_WAVES 2
+#endif
+constexpr int kEStages = PA_EXTEND_STAGES;
+
 constexpr float kExtRescaleSlack = 8.0f;  // log2 units, as in decode
 
 __device__ __forceinline__ int shfl_xor_i(int x, int mask) {
@@ -55,13 +70,13 @@ __device__ __forceinline__ int shfl_xor_i(int x, int mask) {
 // PREFIX = false: extend (chunk of new tokens, causal after the prefix).
 // PREFIX = true:  shared-prefix pass of the cascade decode.
 template <int D, int G, bool PREFIX>
-__global__ __launch_bounds__(kThreads) void mfma_attn_kernel(const ExtendArgs p) {
+__global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(const ExtendArgs p) {
   using C = ExtCfg<D>;
   constexpr int TOK = kRows / G;  // tokens (or group members) per work-group
   constexpr int KSTEPS = C::KSTEPS, DT = C::DT, PPR = C::PPR, NDMA = C::NDMA;
 
-  __shared__ uint4 s_k[kStages][kKT * PPR];
-  __shared__ uint4 s_v[kStages][kKT * PPR];
+  __shared__ uint4 s_k[kEStages][kKT * PPR];
+  __shared__ uint4 s_v[kEStages][kKT * PPR];
   __shared__ int32_t s_pages[kPageCap];
   __shared__ int32_t s_red[2][4];
 
@@ -202,34 +217,29 @@ __global__ __launch_bounds__(kThreads) void mfma_attn_kernel(const ExtendArgs p)
   const float sl2 = p.scale_log2;
   const float slack = kExtRescaleSlack / sl2;  // the same slack in raw-score units
 
-  // ---- prologue: page ids, then tiles 0 and 1 in flight
+  // ---- prologue: page ids, then tiles 0 .. kEStages - 2 in flight
   int chunk = chunk_of(0);
   stage_pages(chunk);
   __syncthreads();
-  issue_tile(0, 0, chunk);
-  if (ntiles > 1) {
-    if (chunk_of(1) != chunk) {  // rare: tile 1 starts the next chunk of page ids
+  for (int t = 0; t < kEStages - 1 && t < ntiles; ++t) {
+    const int c = chunk_of(t);
+    if (c != chunk) {  // rare: the tile starts the next chunk of page ids
       vm_wait<0>();
       __syncthreads();
-      chunk = chunk_of(1);
+      chunk = c;
       stage_pages(chunk);
       __syncthreads();
-      issue_tile(1, 1, chunk);
-      vm_wait<2 * NDMA>();
-    } else {
-      issue_tile(1, 1, chunk);
-      vm_wait<2 * NDMA>();
     }
-  } else {
-    vm_wait<0>();
+    issue_tile(t, t, chunk);
   }
+  wait_next<kEStages, NDMA>(min(kEStages - 2, ntiles - 1));
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t % kStages;
-    const bool ahead = (t + 2) < ntiles;
-    if (ahead) {
-      const int c2 = chunk_of(t + 2);
+    const int buf = t % kEStages;
+    const int tn = t + kEStages - 1;  // the tile issued now
+    if (tn < ntiles) {
+      const int c2 = chunk_of(tn);
       if (c2 != chunk) {  // block-uniform and rare: restage page ids
         vm_wait<0>();
         __syncthreads();
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void mfma_attn_kernel(const ExtendArgs p)
         chunk = c2;
         __syncthreads();
       }
-      issue_tile(t + 2, (t + 2) % kStages, chunk);
+      issue_tile(tn, tn % kEStages, chunk);
     }
 
     // ---- S^T = K Q^T for two 32-key halves of the tile
@@ -322,9 +332,10 @@ __global__ __launch_bounds__(kThreads) void mfma_attn_kernel(const ExtendArgs p)
       }
     }
 
-    // tile t+1 must have landed (tile t+2 may still be in flight) before the
-    // next iteration reads it; the barrier also retires this tile's reads
-    if (ahead) vm_wait<2 * NDMA>(); else vm_wait<0>();
+    // tile t+1 must have landed (the tiles issued after it may still be in
+    // flight) before the next iteration reads it; the barrier also retires
+    // this tile's reads
+    wait_next<kEStages, NDMA>(min(kEStages - 2, ntiles - 2 - t));
     __syncthreads();
   }
 

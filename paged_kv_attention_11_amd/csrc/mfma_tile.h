@@ -41,7 +41,6 @@ struct ExtCfg {
   static_assert(NDMA >= 1 && kKT * PPR % kTileThreads == 0, "bad tile");
 };
 
-constexpr int kStages = 3;      // LDS ring depth: tiles t (computed), t+1, t+2 (in flight)
 constexpr int kPageCap = 1024;  // page ids staged in LDS at a time
 
 // K rows: 16-byte piece p of key k is stored at piece p ^ (k mod PPR), so the
@@ -67,6 +66,27 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* gptr) {
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until the next tile of an S-stage ring has landed while the `after`
+// tiles issued behind it (at most S - 2; fewer near the end) stay in flight.
+// NDMA: direct-to-LDS loads per thread per tile and tensor (K and V: 2 NDMA).
+template <int S, int NDMA>
+__device__ __forceinline__ void wait_next(int after) {
+  static_assert(S >= 2 && S <= 4, "ring depth");
+  if constexpr (S >= 4) {
+    if (after >= 2) {
+      vm_wait<4 * NDMA>();
+      return;
+    }
+  }
+  if constexpr (S >= 3) {
+    if (after >= 1) {
+      vm_wait<2 * NDMA>();
+      return;
+    }
+  }
+  vm_wait<0>();
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));

@@ -56,16 +56,6 @@ __device__ __forceinline__ f32x4_t mfma16_k16(const uint2& a, const uint2& b, co
 #endif
 constexpr int kVStages = PA_VERIFY_STAGES;
 
-// Wait until tile t + 1 has landed while the tiles issued after it (at most
-// kVStages - 2, fewer near the end) stay in flight.
-template <int NDMA>
-__device__ __forceinline__ void wait_next(int after) {
-  if constexpr (kVStages >= 4) {
-    if (after >= 2) { vm_wait<4 * NDMA>(); return; }
-  }
-  if (after >= 1) vm_wait<2 * NDMA>(); else vm_wait<0>();
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   using C = ExtCfg<D>;
@@ -166,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
 
   // ---- prologue: tiles 0 .. kVStages - 2 in flight, tile 0 landed
   for (int t = 0; t < kVStages - 1 && t < ntiles; ++t) issue_tile(t, t);
-  wait_next<NDMA>(min(kVStages - 2, ntiles - 1));
+  wait_next<kVStages, NDMA>(min(kVStages - 2, ntiles - 1));
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -251,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
     }
 
     // tiles issued after t + 1: min(kVStages - 2, ntiles - 2 - t)
-    wait_next<NDMA>(min(kVStages - 2, ntiles - 2 - t));
+    wait_next<kVStages, NDMA>(min(kVStages - 2, ntiles - 2 - t));
     __syncthreads();
   }
 

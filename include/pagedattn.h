@@ -376,6 +376,37 @@ pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_h
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_check_batch: debug check of the device-resident values every other call
+ * takes on trust.  Enqueues kernels that clear *flags (one uint32 in device
+ * memory) and then OR into it:
+ *   PA_CHECK_SEQ_LEN        a seq_len outside [0, max_seq_len]
+ *   PA_CHECK_Q_INDPTR       q_indptr[0] != 0, or a chunk n_b = q_indptr[b+1] -
+ *                           q_indptr[b] outside [0, min(seq_len, max_q_len)]
+ *                           (only when q_indptr is given)
+ *   PA_CHECK_PAGE_ID        a page id outside [0, num_pages) among the
+ *                           ceil(seq_len / page_size) pages a request uses
+ *   PA_CHECK_SLOT_RANGE     a slot >= num_pages * page_size (only when
+ *                           slot_mapping is given)
+ *   PA_CHECK_SLOT_DUPLICATE a live slot given twice (pairwise comparison:
+ *                           meant for debugging, not every step)
+ * It reads only page_table, seq_lens, q_indptr and slot_mapping -- never a
+ * pool page -- so it is safe to run on the very inputs it is meant to catch.
+ * The caller reads *flags after synchronising the stream; 0 means none found.
+ * q_indptr and slot_mapping may be NULL (those checks are skipped).
+ */
+enum {
+  PA_CHECK_SEQ_LEN = 1u,
+  PA_CHECK_Q_INDPTR = 2u,
+  PA_CHECK_PAGE_ID = 4u,
+  PA_CHECK_SLOT_RANGE = 8u,
+  PA_CHECK_SLOT_DUPLICATE = 16u
+};
+pa_status pa_check_batch(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const int32_t* q_indptr,
+                         int32_t max_q_len, const int64_t* slot_mapping, int64_t num_rows, uint32_t* flags,
+                         void* stream);
+
+/*
  * pa_gather: copy the first seq_lens[b] tokens of every request, in logical
  * order, to contiguous k_out / v_out rows starting at row out_offsets[b]
  * (int64 [num_seqs + 1], device).  k_out, v_out: [out_offsets[num_seqs],

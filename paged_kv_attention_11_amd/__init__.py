@@ -82,6 +82,7 @@ SIGNATURES = {
                                _vp]),
     "pa_verify_workspace_bytes": (_sz, [_i32] * 7),
     "pa_verify": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
+    "pa_check_batch": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i64, _vp, _vp]),
     "pa_gather": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
 }
 
@@ -417,6 +418,29 @@ def verify(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, max_seq
                           _stream(stream))
     _check(st, "pa_verify")
     return out
+
+
+CHECK_BITS = {1: "seq_len", 2: "q_indptr", 4: "page_id", 8: "slot_range", 16: "slot_duplicate"}
+
+
+def check_batch(k_pool, v_pool, page_table, seq_lens, max_seq_len, q_indptr=None, max_q_len=0, slot_mapping=None,
+                stream=None):
+    """Debug check of the device-resident batch description; synchronises and
+    returns the names of the violations found (empty: none)."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(q_indptr, "q_indptr", torch.int32)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    flags = torch.empty(1, dtype=torch.int32, device=k_pool.device)
+    n_rows = 0 if slot_mapping is None else slot_mapping.numel()
+    st = load().pa_check_batch(ctypes.byref(pool), _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                               seq_lens.numel(), int(max_seq_len), _ptr(q_indptr), int(max_q_len),
+                               _ptr(slot_mapping), n_rows, _ptr(flags), _stream(stream))
+    _check(st, "pa_check_batch")
+    word = int(flags.item()) & 0xFFFFFFFF
+    return sorted(name for bit, name in CHECK_BITS.items() if word & bit)
 
 
 def gather(k_pool, v_pool, page_table, seq_lens, out_offsets, max_seq_len, k_out, v_out, stream=None):

@@ -586,6 +586,33 @@ pa_status pa_verify(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   return hip_status(pa::launch_verify(a, (hipStream_t)stream));
 }
 
+pa_status pa_check_batch(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const int32_t* q_indptr,
+                         int32_t max_q_len, const int64_t* slot_mapping, int64_t num_rows, uint32_t* flags,
+                         void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || pt_stride < 0 || max_seq_len < 0 || max_q_len < 0 || num_rows < 0) return PA_ERR_SHAPE;
+  if (!flags) return PA_ERR_NULL;
+  if (!aligned(flags, 4)) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!page_table || !seq_lens)) return PA_ERR_NULL;
+  if (num_rows > 0 && !slot_mapping) return PA_ERR_NULL;
+  pa::CheckArgs a;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.q_indptr = q_indptr;
+  a.slot_mapping = num_rows > 0 ? slot_mapping : nullptr;
+  a.flags = flags;
+  a.num_pages = pool->num_pages;
+  a.num_rows = num_rows;
+  a.pt_stride = pt_stride;
+  a.num_seqs = num_seqs;
+  a.max_seq_len = max_seq_len;
+  a.max_q_len = max_q_len;
+  a.page_size = pool->page_size;
+  return hip_status(pa::launch_check(a, (hipStream_t)stream));
+}
+
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
                     const int32_t* seq_lens, const int64_t* out_offsets, int32_t num_seqs,
                     int32_t max_seq_len, void* k_out, void* v_out, void* stream) {

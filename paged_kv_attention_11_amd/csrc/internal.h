@@ -142,6 +142,21 @@ struct VerifyArgs {
   float scale_log2;
 };
 
+struct CheckArgs {
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* q_indptr;      // may be null
+  const int64_t* slot_mapping;  // may be null
+  uint32_t* flags;
+  int64_t num_pages;
+  int64_t num_rows;
+  int32_t pt_stride;
+  int32_t num_seqs;
+  int32_t max_seq_len;
+  int32_t max_q_len;
+  int32_t page_size;
+};
+
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_rope_store(const RopeArgs& a, hipStream_t stream);
@@ -152,5 +167,6 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const ExtendArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 
 }  // namespace pa

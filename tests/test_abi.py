@@ -291,3 +291,16 @@ def test_verify_workspace_size():
     expect = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 8192, 1024) == expect
     assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 1000, 1024) == 0  # one piece: no workspace
+
+
+def test_check_batch_validation():
+    lib = pa.load()
+    p = pool()
+    call = lambda pt=FAKE, sl=FAKE, B=4, qi=0, sm=0, n=0, flags=FAKE: lib.pa_check_batch(
+        ctypes.byref(p), pt, 64, sl, B, 1000, qi, 8, sm, n, flags, None)
+    assert call(flags=0) == NULL
+    assert call(pt=0) == NULL
+    assert call(sl=0) == NULL
+    assert call(n=4) == NULL  # rows without a slot mapping
+    assert call(B=-1) == SHAPE
+    assert call(flags=FAKE + 2) == SHAPE

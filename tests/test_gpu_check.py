@@ -1,0 +1,59 @@
+"""The debug check of device-resident inputs: a valid batch reports nothing,
+and each planted violation (made on the host, in the tables only: no kernel
+that reads pool pages ever sees them) reports its own bit."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_helpers import fresh, pa, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check(wl, dw, page_table=None, seq_lens=None, q_indptr=None, slots=None, max_q_len=None):
+    T = torch()
+    dev = lambda x, dt: T.from_numpy(np.ascontiguousarray(x).astype(dt)).cuda()
+    pt = dw.page_table if page_table is None else dev(page_table, np.int32)
+    sl = dw.seq_lens if seq_lens is None else dev(seq_lens, np.int32)
+    qi = dw.q_indptr if q_indptr is None else dev(q_indptr, np.int32)
+    sm = dw.slot_mapping if slots is None else dev(slots, np.int64)
+    return pa().check_batch(dw.k_pool, dw.v_pool, pt, sl, wl.max_seq_len, q_indptr=qi,
+                            max_q_len=max_q_len or wl.max_q_len, slot_mapping=sm)
+
+
+def test_valid_batches_report_nothing():
+    banner("check: valid batches")
+    for name in ("qwen25_05b", "qwen3_06b_p1", "qwen3_8b_extend"):
+        wl = W.make(name)
+        assert check(wl, fresh(wl)) == [], name
+
+
+def test_each_violation_sets_its_bit():
+    banner("check: planted violations")
+    wl = W.make_custom([40, 300, 17, 1000], 8, 2, 128, 16, dtype="bf16", kind="extend", n_new=[5, 1, 17, 64],
+                       seed=800)
+    dw = fresh(wl)
+    assert check(wl, dw) == []
+    sl = wl.seq_lens.copy(); sl[2] = wl.max_seq_len + 1
+    assert check(wl, dw, seq_lens=sl) == ["seq_len"]
+    sl = wl.seq_lens.copy(); sl[0] = -3
+    assert "seq_len" in check(wl, dw, seq_lens=sl)
+    pt = wl.page_table.copy(); pt[1, 5] = wl.num_pages
+    assert check(wl, dw, page_table=pt) == ["page_id"]
+    pt = wl.page_table.copy(); pt[3, 0] = -1
+    assert check(wl, dw, page_table=pt) == ["page_id"]
+    pt = wl.page_table.copy(); pt[0, pt.shape[1] - 1] = -7  # beyond the request's pages: not read, not reported
+    assert check(wl, dw, page_table=pt) == []
+    qi = wl.q_indptr.copy(); qi[1] = qi[2] + 1  # a negative chunk
+    assert "q_indptr" in check(wl, dw, q_indptr=qi)
+    assert check(wl, dw, max_q_len=32) == ["q_indptr"]  # a chunk of 64 rows above the bound
+    sm = wl.slot_mapping.copy(); sm[3] = wl.num_pages * wl.page_size
+    assert check(wl, dw, slots=sm) == ["slot_range"]
+    sm = wl.slot_mapping.copy(); sm[10] = sm[50]
+    assert check(wl, dw, slots=sm) == ["slot_duplicate"]
+    sm = wl.slot_mapping.copy(); sm[10] = -1; sm[50] = -1  # padding twice is fine
+    assert check(wl, dw, slots=sm) == []

@@ -235,108 +235,129 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
   wait_next<kEStages, NDMA>(min(kEStages - 2, ntiles - 1));
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t % kEStages;
-    const int tn = t + kEStages - 1;  // the tile issued now
-    if (tn < ntiles) {
-      const int c2 = chunk_of(tn);
-      if (c2 != chunk) {  // block-uniform and rare: restage page ids
-        vm_wait<0>();
-        __syncthreads();
-        stage_pages(c2);
-        chunk = c2;
-        __syncthreads();
-      }
-      issue_tile(tn, tn % kEStages, chunk);
-    }
+  // Per-lane LDS byte offsets inside a tile, computed once.  K piece
+  // (2 ks + half) ^ (key mod PPR) of key 32 kt + col sits at
+  // 32 kt PPR 16 + koff[ks]; the transposing V read of step (ks, r) and
+  // head-dim block i sits at 16 ks PPR 16 + 8 r PPR 16 + voff[i].  Together
+  // with a compile-time ring slot the rest of each LDS address is an
+  // instruction's immediate offset.
+  uint32_t koff[KSTEPS], voff[DT];
+  {
+    const int ck = col & (PPR - 1);
+    const int kb = col * PPR * 16 + 16 * (half ^ (ck & 1));
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = kb + 32 * (ks ^ (ck >> 1));
+    const int j = lane & 15, g1 = (lane >> 4) & 1;
+    const int sv = 2 * ((j >> 2) & 3);
+    const int pl = (4 * half + (j >> 2)) * PPR * 16 + 8 * (j & 1) + 16 * ((2 * g1 + ((j >> 1) & 1)) ^ (sv & 3));
+#pragma unroll
+    for (int i = 0; i < DT; ++i) voff[i] = pl + 64 * (i ^ (sv >> 2));
+  }
+  constexpr int kTileBytes = kKT * PPR * 16;
+  const char* const k_lds = (const char*)&s_k[0][0];
+  const char* const v_lds = (const char*)&s_v[0][0];
 
-    // ---- S^T = K Q^T for two 32-key halves of the tile
-    f32x16_t s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      const int key = kt * 32 + col;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const uint4 a = s_k[buf][key * PPR + ((2 * ks + half) ^ k_swz<D>(key))];
-        s[kt] = mfma32(a, qreg[ks], s[kt]);
+  // One tile; `buf` is a compile-time ring slot in every inlined copy.
+  auto tile_step = [&](const int t, const int buf) __attribute__((always_inline)) {
+      const int tn = t + kEStages - 1;  // the tile issued now
+      if (tn < ntiles) {
+        const int c2 = chunk_of(tn);
+        if (c2 != chunk) {  // block-uniform and rare: restage page ids
+          vm_wait<0>();
+          __syncthreads();
+          stage_pages(c2);
+          chunk = c2;
+          __syncthreads();
+        }
+        issue_tile(tn, (buf + kEStages - 1) % kEStages, chunk);
       }
-    }
 
-    // ---- mask, only on tiles that reach past some row's last visible key
-    const int kt0 = k_begin + t * kKT;
-    if (kt0 + kKT - 1 > min_vis) {
+      // ---- S^T = K Q^T for two 32-key halves of the tile
+      f32x16_t s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const uint4 a = *(const uint4*)(k_lds + buf * kTileBytes + kt * 32 * PPR * 16 + koff[ks]);
+          s[kt] = mfma32(a, qreg[ks], s[kt]);
+        }
+      }
+
+      // ---- mask, only on tiles that reach past some row's last visible key
+      const int kt0 = k_begin + t * kKT;
+      if (kt0 + kKT - 1 > min_vis) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key > vis_lim) s[kt][r] = -INFINITY;
+          }
+      }
+
+      // ---- online softmax (lane owns one query row, half of the tile's keys);
+      // the reference maximum moves only when exceeded by the slack
+      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > vis_lim) s[kt][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (lane owns one query row, half of the tile's keys);
-    // the reference maximum moves only when exceeded by the slack
-    float mx = -INFINITY;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      if (__ballot(mx > m_ref + slack) != 0) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < DT; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (__ballot(mx > m_ref + slack) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-    }
-    // a row with no visible key yet keeps weights exp2(-inf) = 0
-    const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
-    uint4 pb[4];  // B operands of the four 16-key steps
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(fmaf(s[kt][r], sl2, mb));
-        l_run += e[r];
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
       }
-      pb[2 * kt + 0] = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
-      pb[2 * kt + 1] =
-          make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
-    }
+      // a row with no visible key yet keeps weights exp2(-inf) = 0
+      const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
+      uint4 pb[4];  // B operands of the four 16-key steps
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          e[r] = fast_exp2(fmaf(s[kt][r], sl2, mb));
+          l_run += e[r];
+        }
+        pb[2 * kt + 0] = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+        pb[2 * kt + 1] =
+            make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
+      }
 
-    // ---- O^T += V^T P^T; the A operand is read transposed out of row-major V:
-    // lane (group of 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims
-    // d0 + 4(j%4) .. +3 and receives V[4 keys][d0 + j]
-    {
-      const int grp = lane >> 4, j = lane & 15;
-      const char* vb = (const char*)&s_v[buf][0];
+      // ---- O^T += V^T P^T; the A operand is read transposed out of row-major V:
+      // lane (group of 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims
+      // d0 + 4(j%4) .. +3 and receives V[4 keys][d0 + j]
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
-        const int d = i * 32 + 16 * (grp & 1) + 4 * (j & 3);
-        const int lp = d >> 3;               // logical 16-byte piece
-        const int within = (d & 4) ? 8 : 0;  // byte offset inside the piece
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int k0 = 16 * ks + 4 * half + (j >> 2);
-          const int k1 = k0 + 8;
-          const uint2 x0 = lds_read_tr16(vb + (k0 * PPR + (lp ^ v_swz<D>(k0))) * 16 + within);
-          const uint2 x1 = lds_read_tr16(vb + (k1 * PPR + (lp ^ v_swz<D>(k1))) * 16 + within);
+          const char* vp = v_lds + buf * kTileBytes + ks * 16 * PPR * 16 + voff[i];
+          const uint2 x0 = lds_read_tr16(vp);
+          const uint2 x1 = lds_read_tr16(vp + 8 * PPR * 16);
           o[i] = mfma32(make_uint4(x0.x, x0.y, x1.x, x1.y), pb[ks], o[i]);
         }
       }
-    }
 
-    // tile t+1 must have landed (the tiles issued after it may still be in
-    // flight) before the next iteration reads it; the barrier also retires
-    // this tile's reads
-    wait_next<kEStages, NDMA>(min(kEStages - 2, ntiles - 2 - t));
-    __syncthreads();
+      // tile t+1 must have landed (the tiles issued after it may still be in
+      // flight) before the next iteration reads it; the barrier also retires
+      // this tile's reads
+      wait_next<kEStages, NDMA>(min(kEStages - 2, ntiles - 2 - t));
+      __syncthreads();
+  };
+
+  for (int t0 = 0; t0 < ntiles; t0 += kEStages) {
+#pragma unroll
+    for (int u = 0; u < kEStages; ++u) {
+      if (t0 + u >= ntiles) break;
+      tile_step(t0 + u, u);
+    }
   }
 
   // ---- normalise and write this lane's row

@@ -276,10 +276,11 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
       f32x16_t s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        // the first step accumulates onto the inline constant 0
+        s[kt] = mfma32(*(const uint4*)(k_lds + buf * kTileBytes + kt * 32 * PPR * 16 + koff[0]), qreg[0],
+                       f32x16_t{});
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
+        for (int ks = 1; ks < KSTEPS; ++ks) {
           const uint4 a = *(const uint4*)(k_lds + buf * kTileBytes + kt * 32 * PPR * 16 + koff[ks]);
           s[kt] = mfma32(a, qreg[ks], s[kt]);
         }
@@ -297,51 +298,51 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
           }
       }
 
-      // ---- online softmax (lane owns one query row, half of the tile's keys);
-      // the reference maximum moves only when exceeded by the slack
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      if (__ballot(mx > m_ref + slack) != 0) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DT; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      }
-      // a row with no visible key yet keeps weights exp2(-inf) = 0
-      const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
-      uint4 pb[4];  // B operands of the four 16-key steps
+      // ---- online softmax and O^T += V^T P^T, one 32-key half at a time so
+      // that the softmax of a half can overlap the matrix-core work of the
+      // other (lane owns one query row; the reference maximum moves only when
+      // exceeded by the slack, checked per half)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        if (__ballot(mx > m_ref + slack) != 0) {
+          const float m_new = fmaxf(m_ref, mx);
+          const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+          m_ref = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < DT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        }
+        // a row with no visible key yet keeps weights exp2(-inf) = 0
+        const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
+        uint4 pb[2];  // B operands of this half's two 16-key steps
         float e[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           e[r] = fast_exp2(fmaf(s[kt][r], sl2, mb));
           l_run += e[r];
         }
-        pb[2 * kt + 0] = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
-        pb[2 * kt + 1] =
-            make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
-      }
+        pb[0] = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+        pb[1] = make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
 
-      // ---- O^T += V^T P^T; the A operand is read transposed out of row-major V:
-      // lane (group of 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims
-      // d0 + 4(j%4) .. +3 and receives V[4 keys][d0 + j]
+        // the A operand is read transposed out of row-major V: lane (group of
+        // 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims d0 + 4(j%4) ..
+        // +3 and receives V[4 keys][d0 + j]
 #pragma unroll
-      for (int i = 0; i < DT; ++i) {
+        for (int i = 0; i < DT; ++i) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const char* vp = v_lds + buf * kTileBytes + ks * 16 * PPR * 16 + voff[i];
-          const uint2 x0 = lds_read_tr16(vp);
-          const uint2 x1 = lds_read_tr16(vp + 8 * PPR * 16);
-          o[i] = mfma32(make_uint4(x0.x, x0.y, x1.x, x1.y), pb[ks], o[i]);
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int ks = 2 * kt + k2;
+            const char* vp = v_lds + buf * kTileBytes + ks * 16 * PPR * 16 + voff[i];
+            const uint2 x0 = lds_read_tr16(vp);
+            const uint2 x1 = lds_read_tr16(vp + 8 * PPR * 16);
+            o[i] = mfma32(make_uint4(x0.x, x0.y, x1.x, x1.y), pb[k2], o[i]);
+          }
         }
       }
 

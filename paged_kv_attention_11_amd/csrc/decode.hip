@@ -104,7 +104,15 @@ template <bool BF16, int D, int G>
 struct DecodeOcc {
   using C = DecodeCfg<BF16, D, G>;
   static constexpr int kEstVgprs = G * C::EPC + (C::NK + C::NV) * 4 * DEPTH + 2 * G + 36;
-  static constexpr int kWaves = 512 / kEstVgprs < 1 ? 1 : (512 / kEstVgprs > 8 ? 8 : 512 / kEstVgprs);
+  static constexpr int kEst = 512 / kEstVgprs < 1 ? 1 : (512 / kEstVgprs > 8 ? 8 : 512 / kEstVgprs);
+  // Corrections where the estimate is too tight, each checked against the
+  // compiler's register report so that no instantiation spills to scratch
+  // memory inside the key loop.
+  static constexpr int kWaves = (BF16 && G == 8)               ? 2
+                                : (BF16 && D == 64 && G == 7)  ? 3
+                                : (D == 64 && G == 5)          ? 4
+                                : (!BF16 && D == 64 && G == 8) ? 3
+                                                               : kEst;
 };
 #ifdef PA_DECODE_MIN_WAVES
 #define PA_DECODE_WAVES(B, D, G) PA_DECODE_MIN_WAVES

@@ -129,6 +129,26 @@ def copy_calibration(iters=10):
     return 2 * nread / (ms * 1e-3) / 1e9, nread, ms
 
 
+def bench_decode_configs(pa, W, torch, np, stream, iters):
+    """pa_decode (partial + combine) on the smaller decode configurations:
+    at these sizes a call is bound by launch and memory latency, not by HBM
+    bandwidth, so the time is the figure of interest."""
+    out = {}
+    for name in ("tiny", "qwen25_05b", "qwen3_06b_p1"):
+        wl = W.make(name)
+        d = W.to_device(wl)
+        pa.kv_store(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slot_mapping)
+        o = torch.empty_like(d.q)
+        ws = pa.decode_workspace(d.q, d.k_pool, wl.max_seq_len)
+        ms = _time(torch, stream, lambda: pa.decode(d.q, d.k_pool, d.v_pool, d.page_table, d.seq_lens, wl.max_seq_len,
+                                                    wl.scale, o, ws), iters)
+        out[name] = {"us": round(ms * 1e3, 2), "GBps_unique": round(wl.kv_bytes_unique() / (ms * 1e-3) / 1e9, 1),
+                     "tokens_per_s": round(wl.num_seqs / (ms * 1e-3), 1), "dtype": wl.dtype,
+                     "description": W.DESCRIPTIONS[name]}
+        del d, ws
+    return out
+
+
 def bench_rope(pa, W, torch, np, stream, iters):
     """pa_rope_kv_store on the chunked-prefill workload's 4096 new rows:
     rotate q (32 heads) and k (8 heads), store k and v.  HBM-bound."""
@@ -523,6 +543,12 @@ def main():
                          "algorithmic_flops_per_launch": flops},
         }
         log(f"extend: {ems * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+
+    # ---------------- the other decode configurations (plain decode, one call)
+    if not args.no_extend:
+        result["decode_configs"] = bench_decode_configs(pa, W, torch, np, stream, max(10, args.steps))
+        log("decode configs: " + ", ".join(f"{k} {v['us']} us ({v['GBps_unique']} GB/s)"
+                                           for k, v in result["decode_configs"].items()))
 
     # ---------------- fused rotary embedding + store (the step before attention)
     if not args.no_extend:

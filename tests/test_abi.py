@@ -304,3 +304,16 @@ def test_check_batch_validation():
     assert call(n=4) == NULL  # rows without a slot mapping
     assert call(B=-1) == SHAPE
     assert call(flags=FAKE + 2) == SHAPE
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: with the library absent every call raises."""
+    import subprocess
+    import sys
+
+    code = ("import paged_kv_attention_11_amd as pa\n"
+            "try:\n    pa.version()\nexcept RuntimeError as e:\n    print('raised', e)\n")
+    env = dict(__import__("os").environ, PAGEDATTN_LIB=str(tmp_path / "absent.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=str(Path(__file__).resolve().parents[1]), timeout=120)
+    assert r.returncode == 0 and "raised" in r.stdout and "absent.so" in r.stdout, r.stdout + r.stderr

@@ -163,7 +163,20 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   const int L = p.seq_lens[b];
   const int k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
   const int t_begin = k0 + s * p.split_tokens;
-  if (t_begin >= L) return;  // uniform over the work-group
+  if (t_begin >= L) {  // uniform over the work-group
+    // a request with no keys gets zero rows here when it has no pieces to
+    // merge later (plain decode)
+    if (s == 0 && L <= 0 && !p.key_begin && !p.always_partial) {
+      const int64_t orow0 = (int64_t)qrow * p.num_q_heads + (int64_t)g * G;
+      for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        if constexpr (BF16)
+          ((uint16_t*)p.out)[orow0 * D + idx] = 0;
+        else
+          ((float*)p.out)[orow0 * D + idx] = 0.f;
+      }
+    }
+    return;
+  }
   const int n_tok = min(L - t_begin, p.split_tokens);
   const int n_splits = (L - k0 + p.split_tokens - 1) / p.split_tokens;
 

@@ -124,11 +124,12 @@ def test_decode_workspace_size_matches_layout():
 
 
 @pytest.mark.parametrize("B,H,L,expect", [
-    (4, 1, 64, 64),        # tiny decode
-    (32, 2, 640, 64),      # Qwen2.5-0.5B shape
-    (64, 8, 2048, 512),    # Qwen3-0.6B shape
+    (4, 1, 64, 64),        # tiny decode: one piece
+    (32, 2, 640, 256),     # Qwen2.5-0.5B shape: too small to fill the chip, 256-key pieces
+    (64, 8, 2048, 256),    # Qwen3-0.6B shape: 512 units x 8 pieces reach 4096 work-groups
     (256, 8, 8192, 1024),  # Qwen3-8B shape
-    (1, 1, 100000, 64),    # one long request: many short pieces fill the chip
+    (1, 8, 65536, 128),    # one long request: 8 heads x 512 pieces
+    (1, 1, 100000, 256),
     (0, 8, 100, 64),
 ])
 def test_automatic_split(B, H, L, expect):

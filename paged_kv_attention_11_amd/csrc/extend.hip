@@ -26,10 +26,16 @@
 //    also accumulated transposed, O^T += V^T P^T, so the rescale factor of a
 //    query row is lane-local and P goes from the score accumulator to the
 //    B operand without leaving registers.
-//  * K and V tiles (64 keys) are copied straight from the pages into an LDS
-//    ring with direct-to-LDS loads one tile ahead, two work-groups per
-//    compute unit (registers cut to 2 waves per SIMD); V stays in row
-//    layout and is read into the A operand with transposing LDS reads.
+//  * K and V are copied straight from the pages into an LDS ring of 32-key
+//    half-tiles with direct-to-LDS loads, a tile ahead, one barrier per
+//    64-key tile; two work-groups per compute unit (registers cut to 2 waves
+//    per SIMD).  V stays in row layout and is read into the A operand with
+//    transposing LDS reads.
+//  * Software pipeline over half-tiles: while the vector units run the
+//    online softmax of half h, the matrix cores take the scores of half h+1
+//    and the PV product of half h-1, interleaved instruction by instruction.
+//  * Work-groups are renumbered so that each XCD runs whole (request, head)
+//    groups, which read the same keys from its L2.
 //  * Key tiles entirely above the diagonal are never visited; only tiles that
 //    cross it (or a row's key limit) are masked.
 //  * Softmax in fp32 (base 2, scale folded with log2 e); P is rounded to bf16
@@ -44,22 +50,23 @@ namespace {
 
 using namespace tile;
 
-constexpr int kThreads = kTileThreads;
-constexpr int kRows = 128;  // query rows per work-group
-
-// LDS ring depth and the waves per SIMD the register budget is cut for.  A
-// 2-stage ring (64 KB for D = 128) with registers cut to 256 lets two
-// work-groups share a compute unit, so one's softmax and LDS traffic overlap
-// the other's matrix-core work: 324 -> 260 us on the Qwen3-8B-shaped
-// chunked-prefill workload, where a deeper ring in one work-group per CU
-// changed nothing.
-#ifndef PA_EXTEND_STAGES
-#define PA_EXTEND_STAGES 2
+// Work-group shape of the two uses of the kernel.  Every wave owns 32 query
+// rows and the waves of a work-group share one LDS ring of K/V.  Both uses
+// run 4 waves, two work-groups per compute unit and two waves per SIMD (the
+// register budget).  On the Qwen3-8B-shaped chunked-prefill workload an
+// earlier, unpipelined version of this kernel measured 251 us with 8 waves
+// (256 rows, half the K/V bytes per FLOP) against 243 us with 4: the tile
+// traffic is not what bounds the kernel.  The shared-prefix pass needs no
+// more: a group of 16 requests x 4 heads is 64 rows.
+#ifndef PA_EXTEND_NW
+#define PA_EXTEND_NW 4
 #endif
-#ifndef PA_EXTEND_WAVES
-#define PA_EXTEND_WAVES 2
-#endif
-constexpr int kEStages = PA_EXTEND_STAGES;
+template <bool PREFIX>
+struct Shape {
+  static constexpr int kWaves = PREFIX ? 4 : PA_EXTEND_NW;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRows = kWaves * 32;
+};
 
 constexpr float kExtRescaleSlack = 8.0f;  // log2 units, as in decode
 
@@ -70,15 +77,21 @@ __device__ __forceinline__ int shfl_xor_i(int x, int mask) {
 // PREFIX = false: extend (chunk of new tokens, causal after the prefix).
 // PREFIX = true:  shared-prefix pass of the cascade decode.
 template <int D, int G, bool PREFIX>
-__global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(const ExtendArgs p) {
+__global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(const ExtendArgs p) {
   using C = ExtCfg<D>;
-  constexpr int TOK = kRows / G;  // tokens (or group members) per work-group
-  constexpr int KSTEPS = C::KSTEPS, DT = C::DT, PPR = C::PPR, NDMA = C::NDMA;
+  using SH = Shape<PREFIX>;
+  constexpr int kThreads = SH::kThreads, kWaves = SH::kWaves;
+  constexpr int TOK = SH::kRows / G;  // tokens (or group members) per work-group
+  constexpr int KSTEPS = C::KSTEPS, DT = C::DT, PPR = C::PPR;
+  constexpr int HB = 32 / C::RPB;  // 1 KB DMA blocks per half-tile and tensor
+  constexpr int NH = HB / kWaves;  // of them per wave
+  static_assert(NH >= 1 && HB % kWaves == 0, "half-tile does not split over the waves");
+  constexpr int kHalfBytes = 32 * PPR * 16;
 
-  __shared__ uint4 s_k[kEStages][kKT * PPR];
-  __shared__ uint4 s_v[kEStages][kKT * PPR];
+  __shared__ uint4 s_k[4][32 * PPR];
+  __shared__ uint4 s_v[4][32 * PPR];
   __shared__ int32_t s_pages[kPageCap];
-  __shared__ int32_t s_red[2][4];
+  __shared__ int32_t s_red[2][kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,14 +105,16 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
   bool qvalid, has_keys;
   const int32_t* pt;
   if constexpr (!PREFIX) {
-    // work-group: token block qb of (request b, KV head g); the blocks of one
-    // (request, head) are consecutive ids, heaviest (latest) first
+    // work-group: token block qb of (request b, KV head g).  The blocks of
+    // one (request, head) are consecutive logical ids, heaviest (latest)
+    // first, then requests, then heads: each XCD runs whole (request, head)
+    // groups, which read the same keys, and a fair mix of requests.
     const int qblocks = (p.max_q_len + TOK - 1) / TOK;
-    int bid = blockIdx.x;
+    int bid = xcd_contiguous(blockIdx.x, gridDim.x);
     const int qb = qblocks - 1 - (bid % qblocks);
     bid /= qblocks;
-    g = bid % p.num_kv_heads;
-    const int b = bid / p.num_kv_heads;
+    const int b = bid % p.num_seqs;
+    g = bid / p.num_seqs;
     const int r0 = p.q_indptr[b];
     const int n = p.q_indptr[b + 1] - r0;
     const int i0 = qb * TOK;
@@ -148,8 +163,13 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
       s_red[1][wave] = mn;
     }
     __syncthreads();
-    mx = max(max(s_red[0][0], s_red[0][1]), max(s_red[0][2], s_red[0][3]));
-    mn = min(min(s_red[1][0], s_red[1][1]), min(s_red[1][2], s_red[1][3]));
+    mx = s_red[0][0];
+    mn = s_red[1][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      mx = max(mx, s_red[0][w]);
+      mn = min(mn, s_red[1][w]);
+    }
     if (k_begin >= mx) return;  // no row of the block reads this piece (uniform)
     k_end = min(k_begin + p.piece_keys, mx);
     min_vis = mn - 1;
@@ -178,34 +198,81 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
   const int64_t row_stride = (int64_t)p.num_kv_heads * D;  // elements per slot
   const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)g * D;
-  const int chunk_keys = kPageCap << sh;  // keys covered by one staging of page ids
+  const uint32_t k_lds0 = lds_addr(&s_k[0][0]), v_lds0 = lds_addr(&s_v[0][0]);
   const int npages = ((k_end - 1) >> sh) + 1;
 
-  // Page ids of chunk c (pages c*kPageCap ...) into LDS; entries past the
-  // block's last page are not read.
-  auto stage_pages = [&](int c) {
-    const int base = c * kPageCap;
+  // Page ids of the window of kPageCap pages starting at page `first` into
+  // LDS; entries past the block's last page are not read.
+  int pwin = k_begin >> sh;
+  auto stage_pages = [&](int first) {
     for (int i = tid; i < kPageCap; i += kThreads)
-      if (base + i < npages) s_pages[i] = pt[base + i];
+      if (first + i < npages) s_pages[i] = pt[first + i];
   };
 
-  // DMA of tile t into ring slot sb: each wave fills NDMA 1 KB blocks of K and
-  // of V.  Keys past the block's range are clamped to its last key (a real
-  // row; masked out of the softmax).
-  auto issue_tile = [&](int t, int sb, int chunk) {
-    const int pc = lane % PPR;
+  // K/V ring: each tensor holds four 32-key half-tiles, half j of tile t in
+  // slot (2t + j) mod 4.  A half is NH 1 KB blocks per wave, one
+  // direct-to-LDS load each; lane l of block hb loads piece l mod PPR of key
+  // hb RPB + l / PPR of the half, from the swizzled position.  Keys past the
+  // block's range are clamped to its last key (a real row; masked out of the
+  // softmax).
+  int hkey[NH];
+  uint32_t kpiece[NH], vpiece[NH];  // byte offsets inside a pool row
 #pragma unroll
-    for (int m = 0; m < NDMA; ++m) {
-      const int blk = wave * NDMA + m;
-      const int key = blk * C::RPB + lane / PPR;
-      const int kk = min(k_begin + t * kKT + key, k_end - 1);
-      const int32_t page = s_pages[(kk >> sh) - chunk * kPageCap];
-      const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride;
-      dma16(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(key)) * 8);
-      dma16(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(key)) * 8);
+  for (int m = 0; m < NH; ++m) {
+    hkey[m] = (wave * NH + m) * C::RPB + lane / PPR;
+    kpiece[m] = (uint32_t)(((lane % PPR) ^ k_swz<D>(hkey[m])) * 16);
+    vpiece[m] = (uint32_t)(((lane % PPR) ^ v_swz<D>(hkey[m])) * 16);
+  }
+  const uint32_t row_bytes = (uint32_t)row_stride * 2u;
+  const char* const kb8 = (const char*)kbase;
+  const char* const vb8 = (const char*)vbase;
+  // byte offsets of the pool rows one half reads: the page lookups first,
+  // then one 32 x 32 -> 64-bit product per block
+  auto half_rows = [&](int t, int j, uint64_t* off) __attribute__((always_inline)) {
+    int kk[NH], pg[NH];
+#pragma unroll
+    for (int m = 0; m < NH; ++m) kk[m] = min(k_begin + t * kKT + j * 32 + hkey[m], k_end - 1);
+#pragma unroll
+    for (int m = 0; m < NH; ++m) pg[m] = s_pages[(kk[m] >> sh) - pwin];
+#pragma unroll
+    for (int m = 0; m < NH; ++m) off[m] = (uint64_t)(uint32_t)((pg[m] << sh) | (kk[m] & pmask)) * row_bytes;
+  };
+  auto dma_half = [&](const bool is_v, const uint64_t* off, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NH; ++m) {
+      const uint32_t lds = (is_v ? v_lds0 : k_lds0) + slot * kHalfBytes + (wave * NH + m) * 1024;
+      dma16(lds, (is_v ? vb8 + vpiece[m] : kb8 + kpiece[m]) + off[m]);
     }
   };
-  auto chunk_of = [&](int t) { return (k_begin + t * kKT) / chunk_keys; };
+  // Row offsets of halves (t, 1) and (t + 1, 0), computed when their K was
+  // issued and used again for their V a tile later.
+  uint64_t c1[NH], c0[NH];
+
+  // Issued right after the barrier that opens tile t (of parity u), to land
+  // by the next one: V(t, 1), K(t+1, 1), V(t+1, 0) and K(t+2, 0).  Their
+  // slots are the four the steps of tile t do not read.
+  auto issue_after = [&](int t, const int u) __attribute__((always_inline)) {
+    const int kmax = min(k_begin + (t + 2) * kKT + 31, k_end - 1);  // no key looked up now is larger
+    if ((kmax >> sh) - pwin >= kPageCap) {  // block-uniform and rare: slide the window
+      pwin = (k_begin + t * kKT + 32) >> sh;  // the smallest key looked up now
+      stage_pages(pwin);
+      __syncthreads();
+    }
+    uint64_t n1[NH], n0[NH];
+    half_rows(t + 1, 1, n1);  // clamped keys when past the last tile
+    half_rows(t + 2, 0, n0);
+    dma_half(true, c1, (2 * u + 1) & 3);
+    if (t + 1 < ntiles) {
+      dma_half(false, n1, (2 * u + 3) & 3);
+      dma_half(true, c0, (2 * u + 2) & 3);
+    }
+    if (t + 2 < ntiles) dma_half(false, n0, (2 * u) & 3);
+#pragma unroll
+    for (int m = 0; m < NH; ++m) {
+      c1[m] = n1[m];
+      c0[m] = n0[m];
+    }
+  };
 
   f32x16_t o[DT];
 #pragma unroll
@@ -217,30 +284,11 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
   const float sl2 = p.scale_log2;
   const float slack = kExtRescaleSlack / sl2;  // the same slack in raw-score units
 
-  // ---- prologue: page ids, then tiles 0 .. kEStages - 2 in flight
-  int chunk = chunk_of(0);
-  stage_pages(chunk);
-  __syncthreads();
-  for (int t = 0; t < kEStages - 1 && t < ntiles; ++t) {
-    const int c = chunk_of(t);
-    if (c != chunk) {  // rare: the tile starts the next chunk of page ids
-      vm_wait<0>();
-      __syncthreads();
-      chunk = c;
-      stage_pages(chunk);
-      __syncthreads();
-    }
-    issue_tile(t, t, chunk);
-  }
-  wait_next<kEStages, NDMA>(min(kEStages - 2, ntiles - 1));
-  __syncthreads();
-
-  // Per-lane LDS byte offsets inside a tile, computed once.  K piece
-  // (2 ks + half) ^ (key mod PPR) of key 32 kt + col sits at
-  // 32 kt PPR 16 + koff[ks]; the transposing V read of step (ks, r) and
-  // head-dim block i sits at 16 ks PPR 16 + 8 r PPR 16 + voff[i].  Together
-  // with a compile-time ring slot the rest of each LDS address is an
-  // instruction's immediate offset.
+  // Per-lane LDS byte offsets inside a half-tile slot, computed once.  K
+  // piece (2 ks + half) ^ (key mod PPR) of key col sits at koff[ks]; the
+  // transposing V read of step (k2, r) and head-dim block i sits at
+  // 16 k2 PPR 16 + 8 r PPR 16 + voff[i].  With a compile-time slot the rest
+  // of each LDS address is an instruction's immediate offset.
   uint32_t koff[KSTEPS], voff[DT];
   {
     const int ck = col & (PPR - 1);
@@ -253,113 +301,160 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
 #pragma unroll
     for (int i = 0; i < DT; ++i) voff[i] = pl + 64 * (i ^ (sv >> 2));
   }
-  constexpr int kTileBytes = kKT * PPR * 16;
   const char* const k_lds = (const char*)&s_k[0][0];
   const char* const v_lds = (const char*)&s_v[0][0];
 
-  // One tile; `buf` is a compile-time ring slot in every inlined copy.
-  auto tile_step = [&](const int t, const int buf) __attribute__((always_inline)) {
-      const int tn = t + kEStages - 1;  // the tile issued now
-      if (tn < ntiles) {
-        const int c2 = chunk_of(tn);
-        if (c2 != chunk) {  // block-uniform and rare: restage page ids
-          vm_wait<0>();
-          __syncthreads();
-          stage_pages(c2);
-          chunk = c2;
-          __syncthreads();
-        }
-        issue_tile(tn, (buf + kEStages - 1) % kEStages, chunk);
+  // S^T = K Q^T for the 32 keys of one half-tile slot (the first k-step
+  // accumulates onto the inline constant 0)
+  auto qk = [&](const int slot) __attribute__((always_inline)) {
+    const char* kp = k_lds + slot * kHalfBytes;
+    f32x16_t sc = mfma32(*(const uint4*)(kp + koff[0]), qreg[0], f32x16_t{});
+#pragma unroll
+    for (int ks = 1; ks < KSTEPS; ++ks) sc = mfma32(*(const uint4*)(kp + koff[ks]), qreg[ks], sc);
+    return sc;
+  };
+  // O^T += V^T P^T for one half-tile slot.  The A operand is read transposed
+  // out of row-major V: lane (group of 16, j) reads keys 16 k2 + 8 r +
+  // 4 half + j/4, head-dims d0 + 4 (j mod 4) .. +3 and receives
+  // V[4 keys][d0 + j].
+  auto pv = [&](const uint4* pb, const int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const char* vp = v_lds + slot * kHalfBytes + k2 * 16 * PPR * 16 + voff[i];
+        const uint2 x0 = lds_read_tr16(vp);
+        const uint2 x1 = lds_read_tr16(vp + 8 * PPR * 16);
+        o[i] = mfma32(make_uint4(x0.x, x0.y, x1.x, x1.y), pb[k2], o[i]);
       }
-
-      // ---- S^T = K Q^T for two 32-key halves of the tile
-      f32x16_t s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        // the first step accumulates onto the inline constant 0
-        s[kt] = mfma32(*(const uint4*)(k_lds + buf * kTileBytes + kt * 32 * PPR * 16 + koff[0]), qreg[0],
-                       f32x16_t{});
-#pragma unroll
-        for (int ks = 1; ks < KSTEPS; ++ks) {
-          const uint4 a = *(const uint4*)(k_lds + buf * kTileBytes + kt * 32 * PPR * 16 + koff[ks]);
-          s[kt] = mfma32(a, qreg[ks], s[kt]);
-        }
-      }
-
-      // ---- mask, only on tiles that reach past some row's last visible key
-      const int kt0 = k_begin + t * kKT;
-      if (kt0 + kKT - 1 > min_vis) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key > vis_lim) s[kt][r] = -INFINITY;
-          }
-      }
-
-      // ---- online softmax and O^T += V^T P^T, one 32-key half at a time so
-      // that the softmax of a half can overlap the matrix-core work of the
-      // other (lane owns one query row; the reference maximum moves only when
-      // exceeded by the slack, checked per half)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        if (__ballot(mx > m_ref + slack) != 0) {
-          const float m_new = fmaxf(m_ref, mx);
-          const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
-          m_ref = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < DT; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-        }
-        // a row with no visible key yet keeps weights exp2(-inf) = 0
-        const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
-        uint4 pb[2];  // B operands of this half's two 16-key steps
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          e[r] = fast_exp2(fmaf(s[kt][r], sl2, mb));
-          l_run += e[r];
-        }
-        pb[0] = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
-        pb[1] = make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
-
-        // the A operand is read transposed out of row-major V: lane (group of
-        // 16, j) reads keys 16ks + 8r + 4*half + j/4, head-dims d0 + 4(j%4) ..
-        // +3 and receives V[4 keys][d0 + j]
-#pragma unroll
-        for (int i = 0; i < DT; ++i) {
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const int ks = 2 * kt + k2;
-            const char* vp = v_lds + buf * kTileBytes + ks * 16 * PPR * 16 + voff[i];
-            const uint2 x0 = lds_read_tr16(vp);
-            const uint2 x1 = lds_read_tr16(vp + 8 * PPR * 16);
-            o[i] = mfma32(make_uint4(x0.x, x0.y, x1.x, x1.y), pb[k2], o[i]);
-          }
-        }
-      }
-
-      // tile t+1 must have landed (the tiles issued after it may still be in
-      // flight) before the next iteration reads it; the barrier also retires
-      // this tile's reads
-      wait_next<kEStages, NDMA>(min(kEStages - 2, ntiles - 2 - t));
-      __syncthreads();
   };
 
-  for (int t0 = 0; t0 < ntiles; t0 += kEStages) {
+  // ---- prologue: page ids; K(0, *), K(1, 0) and V(0, 0) in, the V slot of
+  // the (empty) half before the first zeroed; scores of half (0, 0)
+  stage_pages(pwin);
+  for (int i = tid; i < 32 * PPR; i += kThreads) s_v[3][i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  {
+    uint64_t h00[NH];
+    half_rows(0, 0, h00);
+    half_rows(0, 1, c1);
+    half_rows(1, 0, c0);  // clamped keys when there is one tile
+    dma_half(false, h00, 0);
+    dma_half(false, c1, 1);
+    dma_half(true, h00, 0);
+    if (ntiles > 1) dma_half(false, c0, 2);
+  }
+  vm_wait<0>();
+  __syncthreads();
+  f32x16_t s_cur = qk(0);
+  uint4 pp[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};  // P of the previous half
+  __syncthreads();  // K slot 0 is refilled next
+
+  // One pipeline step on half (t, j), whose scores are in s_cur: its online
+  // softmax on the vector units while the matrix cores take the next half's
+  // scores (K slot kslot) and the previous half's product (V slot vslot).
+  // The reference maximum moves only when a score passes it by the slack;
+  // the rescale of O then follows the previous half's product, which was
+  // weighted against the old reference.
+  auto step = [&](const bool masked, const int t, const int j, const int kslot, const int vslot)
+                  __attribute__((always_inline)) {
+    if (masked) {  // block-uniform; only on halves that reach past a row's last key
+      const int kb = k_begin + t * kKT + j * 32;
 #pragma unroll
-    for (int u = 0; u < kEStages; ++u) {
-      if (t0 + u >= ntiles) break;
-      tile_step(t0 + u, u);
+      for (int r = 0; r < 16; ++r)
+        if (kb + 8 * (r >> 2) + 4 * half + (r & 3) > vis_lim) s_cur[r] = -INFINITY;
+    }
+    float mx = s_cur[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+    {  // lanes l and l ^ 32 hold the two halves of a row: swap and take both
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool grow = __ballot(mx > m_ref + slack) != 0;  // wave-uniform
+    const float m_use = grow ? fmaxf(m_ref, mx) : m_ref;
+    // a row with no visible key yet keeps weights exp2(-inf) = 0
+    const float mb = m_use == -INFINITY ? 0.f : -m_use * sl2;
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s_cur[r], sl2, mb));
+    const uint4 pc0 = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+    const uint4 pc1 = make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
+    // the row sum takes the weights as rounded for the product
+    constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
+    float ls = dot2_bf16(pc0.x, kOnes, 0.f);
+    ls = dot2_bf16(pc0.y, kOnes, ls);
+    ls = dot2_bf16(pc0.z, kOnes, ls);
+    ls = dot2_bf16(pc0.w, kOnes, ls);
+    ls = dot2_bf16(pc1.x, kOnes, ls);
+    ls = dot2_bf16(pc1.y, kOnes, ls);
+    ls = dot2_bf16(pc1.z, kOnes, ls);
+    ls = dot2_bf16(pc1.w, kOnes, ls);
+
+    // matrix-core work, the two chains alternating: k-step k of the next
+    // half's scores, then product step k of the previous half (head-dim
+    // block k / 2, 16-key step k mod 2)
+    static_assert(KSTEPS == 2 * DT, "one product step per score k-step");
+    const char* kp = k_lds + kslot * kHalfBytes;
+    f32x16_t s_nxt;
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      const uint4 ka = *(const uint4*)(kp + koff[k]);
+      s_nxt = k == 0 ? mfma32(ka, qreg[0], f32x16_t{}) : mfma32(ka, qreg[k], s_nxt);
+      const int i = k >> 1, k2 = k & 1;
+      const char* vp = v_lds + vslot * kHalfBytes + k2 * 16 * PPR * 16 + voff[i];
+      const uint2 x0 = lds_read_tr16(vp);
+      const uint2 x1 = lds_read_tr16(vp + 8 * PPR * 16);
+      o[i] = mfma32(make_uint4(x0.x, x0.y, x1.x, x1.y), pp[k2], o[i]);
+    }
+    // Order: the operands of the first two MFMA pairs, then each MFMA
+    // followed by the LDS reads (three per pair, issued two pairs ahead) and
+    // the vector work that fit under it.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // vector ALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // vector ALU
+    }
+    // the weights are formed before the (rare) rescale branch below
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pc0)), "v"(__builtin_bit_cast(u32x4_t, pc1)), "v"(ls));
+    if (grow) {
+      const float alpha = m_use == -INFINITY ? 1.f : fast_exp2((m_ref - m_use) * sl2);
+      m_ref = m_use;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+    l_run += ls;
+    pp[0] = pc0;
+    pp[1] = pc1;
+    s_cur = s_nxt;
+  };
+
+  for (int t0 = 0; t0 < ntiles; t0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = t0 + u;
+      if (t >= ntiles) break;
+      issue_after(t, u);
+      const int kt0 = k_begin + t * kKT;
+      // half (t, 0): scores of (t, 1), product of (t - 1, 1)
+      step(kt0 + 31 > min_vis, t, 0, 2 * u + 1, (2 * u + 3) & 3);
+      // half (t, 1): scores of (t + 1, 0) (unused after the last tile),
+      // product of (t, 0)
+      step(kt0 + kKT - 1 > min_vis, t, 1, (2 * u + 2) & 3, 2 * u);
+      // this tile's DMA has landed everywhere and its slots' readers are done
+      vm_wait<0>();
+      __syncthreads();
     }
   }
+  pv(pp, (2 * ntiles - 1) & 3);  // product of the last half
 
   // ---- normalise and write this lane's row
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
@@ -398,11 +493,12 @@ __global__ __launch_bounds__(kThreads, PA_EXTEND_WAVES) void mfma_attn_kernel(co
 
 template <int D, int G, bool PREFIX>
 hipError_t launch_g(const ExtendArgs& a, hipStream_t stream) {
-  constexpr int TOK = kRows / G;
+  constexpr int TOK = Shape<PREFIX>::kRows / G;
   const int64_t blocks_per = (a.max_q_len + TOK - 1) / TOK;
   const int64_t blocks = blocks_per * a.num_kv_heads * a.num_seqs * (PREFIX ? a.num_pieces : 1);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma_attn_kernel<D, G, PREFIX>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((mfma_attn_kernel<D, G, PREFIX>), dim3((unsigned)blocks), dim3(Shape<PREFIX>::kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

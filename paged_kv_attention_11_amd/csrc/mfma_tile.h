@@ -105,5 +105,15 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* ptr) {
 #endif
 }
 
+// Work-group ids go to the chip's 8 XCDs in turn (id i to XCD i mod 8).
+// Renumbered by this bijection, XCD x runs one contiguous range of logical
+// ids, in order, so work-groups that read the same keys share its L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
+  constexpr int kXcds = 8;
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  const int x = bid % kXcds, local = bid / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
 }  // namespace tile
 }  // namespace pa

@@ -68,7 +68,9 @@ struct Shape {
   static constexpr int kRows = kWaves * 32;
 };
 
-constexpr float kExtRescaleSlack = 8.0f;  // log2 units, as in decode
+// Largest row sum (one lane's 16 weights) the usual path of the online
+// softmax accepts against its reference; beyond it the reference moves.
+constexpr float kMaxRowSum = 65536.0f;
 
 __device__ __forceinline__ int shfl_xor_i(int x, int mask) {
   return __builtin_amdgcn_ds_bpermute((__lane_id() ^ mask) << 2, x);
@@ -108,18 +110,45 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     // work-group: token block qb of (request b, KV head g).  The blocks of
     // one (request, head) are consecutive logical ids, heaviest (latest)
     // first, then requests, then heads: each XCD runs whole (request, head)
-    // groups, which read the same keys, and a fair mix of requests.
+    // groups, which read the same keys, and a fair mix of requests.  In a
+    // batch of at most 64 requests, the requests go in order of decreasing
+    // key count, so that the longest work-groups start first and the
+    // shortest fill the end.
     const int qblocks = (p.max_q_len + TOK - 1) / TOK;
     int bid = xcd_contiguous(blockIdx.x, gridDim.x);
     const int qb = qblocks - 1 - (bid % qblocks);
     bid /= qblocks;
-    const int b = bid % p.num_seqs;
+    int b = bid % p.num_seqs;
     g = bid / p.num_seqs;
-    const int r0 = p.q_indptr[b];
-    const int n = p.q_indptr[b + 1] - r0;
+    int r0, n, L;
+    if (p.num_seqs <= 64) {
+      // lane j: request j's row range and cost (its key count; -1 when the
+      // request runs no work-group here); ties keep the request order
+      int cost = INT_MIN, rj = 0, nj = 0, lj = 0;
+      if (lane < p.num_seqs) {
+        rj = p.q_indptr[lane];
+        nj = p.q_indptr[lane + 1] - rj;
+        lj = p.seq_lens[lane];
+        cost = (nj > 1 || (nj == 1 && !p.skip_single)) ? lj : -1;
+      }
+      int sel = b;
+      for (int i = 0; i < p.num_seqs; ++i) {  // uniform loop
+        const int ci = __builtin_amdgcn_readlane(cost, i);
+        const int rank = __popcll(__ballot(cost > ci)) + __popcll(__ballot(cost == ci) & ((1ull << i) - 1));
+        if (rank == b) sel = i;
+      }
+      b = sel;
+      r0 = __builtin_amdgcn_readlane(rj, b);
+      n = __builtin_amdgcn_readlane(nj, b);
+      L = __builtin_amdgcn_readlane(lj, b);
+    } else {
+      r0 = p.q_indptr[b];
+      n = p.q_indptr[b + 1] - r0;
+      L = p.seq_lens[b];
+    }
     const int i0 = qb * TOK;
     if (i0 >= n || (n == 1 && p.skip_single)) return;
-    const int prefix = p.seq_lens[b] - n;
+    const int prefix = L - n;
     k_begin = 0;
     k_end = prefix + min(i0 + TOK, n);  // keys this block can see
     const int ti = i0 + (row % TOK);
@@ -241,7 +270,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
 #pragma unroll
     for (int m = 0; m < NH; ++m) {
       const uint32_t lds = (is_v ? v_lds0 : k_lds0) + slot * kHalfBytes + (wave * NH + m) * 1024;
-      dma16(lds, (is_v ? vb8 + vpiece[m] : kb8 + kpiece[m]) + off[m]);
+      dma16_unordered(lds, (is_v ? vb8 + vpiece[m] : kb8 + kpiece[m]) + off[m]);
     }
   };
   // Row offsets of halves (t, 1) and (t + 1, 0), computed when their K was
@@ -249,24 +278,26 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   uint64_t c1[NH], c0[NH];
 
   // Issued right after the barrier that opens tile t (of parity u), to land
-  // by the next one: V(t, 1), K(t+1, 1), V(t+1, 0) and K(t+2, 0).  Their
-  // slots are the four the steps of tile t do not read.
-  auto issue_after = [&](int t, const int u) __attribute__((always_inline)) {
+  // by the next one: V(t, 1), K(t+1, 1), V(t+1, 0)
+  // and K(t+2, 0).  Their slots are the four the steps of tile t do not
+  // read, so the loads past the last tile (clamped keys, never read) are
+  // issued too and the issue has no branch.
+  auto slide_window = [&](int t) __attribute__((always_inline)) {
     const int kmax = min(k_begin + (t + 2) * kKT + 31, k_end - 1);  // no key looked up now is larger
-    if ((kmax >> sh) - pwin >= kPageCap) {  // block-uniform and rare: slide the window
+    if ((kmax >> sh) - pwin >= kPageCap) {  // block-uniform and rare
       pwin = (k_begin + t * kKT + 32) >> sh;  // the smallest key looked up now
       stage_pages(pwin);
       __syncthreads();
     }
+  };
+  auto issue_after = [&](int t, const int u) __attribute__((always_inline)) {
     uint64_t n1[NH], n0[NH];
-    half_rows(t + 1, 1, n1);  // clamped keys when past the last tile
+    half_rows(t + 1, 1, n1);
     half_rows(t + 2, 0, n0);
     dma_half(true, c1, (2 * u + 1) & 3);
-    if (t + 1 < ntiles) {
-      dma_half(false, n1, (2 * u + 3) & 3);
-      dma_half(true, c0, (2 * u + 2) & 3);
-    }
-    if (t + 2 < ntiles) dma_half(false, n0, (2 * u) & 3);
+    dma_half(false, n1, (2 * u + 3) & 3);
+    dma_half(true, c0, (2 * u + 2) & 3);
+    dma_half(false, n0, (2 * u) & 3);
 #pragma unroll
     for (int m = 0; m < NH; ++m) {
       c1[m] = n1[m];
@@ -282,7 +313,6 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   float m_ref = -INFINITY;  // reference maximum of this row's raw scores
   float l_run = 0.f;        // this lane's half of the running sum
   const float sl2 = p.scale_log2;
-  const float slack = kExtRescaleSlack / sl2;  // the same slack in raw-score units
 
   // Per-lane LDS byte offsets inside a half-tile slot, computed once.  K
   // piece (2 ks + half) ^ (key mod PPR) of key col sits at koff[ks]; the
@@ -296,7 +326,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = kb + 32 * (ks ^ (ck >> 1));
     const int j = lane & 15, g1 = (lane >> 4) & 1;
-    const int sv = 2 * ((j >> 2) & 3);
+    const int sv = v_swz<D>(j >> 2);  // keys read here are j/4 mod 4
     const int pl = (4 * half + (j >> 2)) * PPR * 16 + 8 * (j & 1) + 16 * ((2 * g1 + ((j >> 1) & 1)) ^ (sv & 3));
 #pragma unroll
     for (int i = 0; i < DT; ++i) voff[i] = pl + 64 * (i ^ (sv >> 2));
@@ -353,9 +383,16 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   // One pipeline step on half (t, j), whose scores are in s_cur: its online
   // softmax on the vector units while the matrix cores take the next half's
   // scores (K slot kslot) and the previous half's product (V slot vslot).
-  // The reference maximum moves only when a score passes it by the slack;
-  // the rescale of O then follows the previous half's product, which was
-  // weighted against the old reference.
+  //
+  // Weights are taken against a per-row reference m_ref, not the running
+  // maximum: any reference gives the same normalised result as long as the
+  // weights stay in range.  The usual path therefore skips the row maximum
+  // and only checks the row sum it forms anyway: a sum above 2^16 (or not
+  // finite -- the first half, when no reference exists yet) sends the wave
+  // to the exact path, which moves the reference to the row maximum,
+  // rescales O and the sum (after the previous half's product, weighted
+  // against the old reference) and forms the weights again.  A row with no
+  // visible key yet takes reference 0; its weights are exp2(-inf) = 0.
   auto step = [&](const bool masked, const int t, const int j, const int kslot, const int vslot)
                   __attribute__((always_inline)) {
     if (masked) {  // block-uniform; only on halves that reach past a row's last key
@@ -364,32 +401,27 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
       for (int r = 0; r < 16; ++r)
         if (kb + 8 * (r >> 2) + 4 * half + (r & 3) > vis_lim) s_cur[r] = -INFINITY;
     }
-    float mx = s_cur[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-    {  // lanes l and l ^ 32 hold the two halves of a row: swap and take both
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const bool grow = __ballot(mx > m_ref + slack) != 0;  // wave-uniform
-    const float m_use = grow ? fmaxf(m_ref, mx) : m_ref;
-    // a row with no visible key yet keeps weights exp2(-inf) = 0
-    const float mb = m_use == -INFINITY ? 0.f : -m_use * sl2;
-    float e[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s_cur[r], sl2, mb));
-    const uint4 pc0 = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
-    const uint4 pc1 = make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
-    // the row sum takes the weights as rounded for the product
     constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
-    float ls = dot2_bf16(pc0.x, kOnes, 0.f);
-    ls = dot2_bf16(pc0.y, kOnes, ls);
-    ls = dot2_bf16(pc0.z, kOnes, ls);
-    ls = dot2_bf16(pc0.w, kOnes, ls);
-    ls = dot2_bf16(pc1.x, kOnes, ls);
-    ls = dot2_bf16(pc1.y, kOnes, ls);
-    ls = dot2_bf16(pc1.z, kOnes, ls);
-    ls = dot2_bf16(pc1.w, kOnes, ls);
+    // weights against reference m, rounded for the product; the row sum
+    // (this lane's half) takes them as rounded
+    auto weigh = [&](float m, uint4& w0, uint4& w1) __attribute__((always_inline)) {
+      const float mb = -m * sl2;
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s_cur[r], sl2, mb));
+      w0 = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+      w1 = make_uint4(pack2(e[8], e[9]), pack2(e[10], e[11]), pack2(e[12], e[13]), pack2(e[14], e[15]));
+      float sum = dot2_bf16(w0.x, kOnes, 0.f);
+      sum = dot2_bf16(w0.y, kOnes, sum);
+      sum = dot2_bf16(w0.z, kOnes, sum);
+      sum = dot2_bf16(w0.w, kOnes, sum);
+      sum = dot2_bf16(w1.x, kOnes, sum);
+      sum = dot2_bf16(w1.y, kOnes, sum);
+      sum = dot2_bf16(w1.z, kOnes, sum);
+      return dot2_bf16(w1.w, kOnes, sum);
+    };
+    uint4 pc0, pc1;
+    float ls = weigh(m_ref, pc0, pc1);
 
     // matrix-core work, the two chains alternating: k-step k of the next
     // half's scores, then product step k of the previous half (head-dim
@@ -415,21 +447,31 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     for (int k = 0; k < KSTEPS; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // vector ALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // vector ALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // vector ALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // vector ALU
     }
-    // the weights are formed before the (rare) rescale branch below
+    // the weights are formed before the (rare) exact path below
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pc0)), "v"(__builtin_bit_cast(u32x4_t, pc1)), "v"(ls));
-    if (grow) {
-      const float alpha = m_use == -INFINITY ? 1.f : fast_exp2((m_ref - m_use) * sl2);
-      m_ref = m_use;
+    if (__ballot(!(ls <= kMaxRowSum)) != 0) {  // wave-uniform
+      float mx = s_cur[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+      {  // lanes l and l ^ 32 hold the two halves of a row: swap and take both
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      float m_new = fmaxf(m_ref, mx);
+      if (m_new == -INFINITY) m_new = 0.f;  // no visible key yet
+      const float alpha = fast_exp2((m_ref - m_new) * sl2);  // 0 when there was no reference
+      m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DT; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      ls = weigh(m_ref, pc0, pc1);
     }
     l_run += ls;
     pp[0] = pc0;
@@ -442,6 +484,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     for (int u = 0; u < 2; ++u) {
       const int t = t0 + u;
       if (t >= ntiles) break;
+      slide_window(t);
       issue_after(t, u);
       const int kt0 = k_begin + t * kKT;
       // half (t, 0): scores of (t, 1), product of (t - 1, 1)

@@ -47,10 +47,18 @@ constexpr int kPageCap = 1024;  // page ids staged in LDS at a time
 // 32 keys read by one MFMA operand fetch hit distinct banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int key) { return key & (ExtCfg<D>::PPR - 1); }
-// V rows: piece p of key k at p ^ 2(k mod 4), so the 4 keys x 32 bytes of one
-// transposing read group fall on distinct banks.
+// V rows: piece p of key k at p ^ v_swz(k).  For D = 128 (four 64-byte
+// blocks per row) the block index is XORed with k mod 4 and the 16-byte
+// chunk with bit 1 of k: the 4 keys x 64 bytes that half a wave reads with
+// one transposing read cover all 256 bytes of the bank space, and any 16
+// lanes cover 128 distinct bytes.  For D = 64, p ^ 2(k mod 4).
 template <int D>
-__device__ __forceinline__ int v_swz(int key) { return (2 * (key & 3)) & (ExtCfg<D>::PPR - 1); }
+__device__ __forceinline__ int v_swz(int key) {
+  if constexpr (ExtCfg<D>::PPR == 16)
+    return 4 * (key & 3) + 2 * ((key >> 1) & 1);
+  else
+    return (2 * (key & 3)) & (ExtCfg<D>::PPR - 1);
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
@@ -62,6 +70,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
 // reads; completion is awaited explicitly with vm_wait below.
 __device__ __forceinline__ void dma16(uint32_t lds, const void* gptr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
+}
+// The same load without a memory clobber, so that the compiler may move
+// ordinary LDS reads across it.  For rings whose slots being filled are never
+// read before the next barrier; ordering against the waits and barriers is
+// kept (both are volatile).
+__device__ __forceinline__ void dma16_unordered(uint32_t lds, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "m0");
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {

@@ -103,51 +103,123 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   const int row = wave * 32 + col;  // rows are (head, token/member) with token fastest
   const int hq = row / TOK;
 
+  // ---- extend: the requests that run work-groups here (more than one row,
+  // or one when single rows are not skipped) first, in order of decreasing
+  // key count when there are at most 64 of them, the others after them;
+  // with their row ranges, once per work-group (batches of at most
+  // kRankMax requests; larger batches keep the request order).
+  constexpr int kRankMax = PREFIX ? 1 : kThreads;
+  __shared__ int32_t s_req[4][kRankMax];  // at position r: request, first row, rows, keys
+  __shared__ int32_t s_cnt[kWaves];
+  bool ranked = false;
+  int n_active = 0;
+  if constexpr (!PREFIX) {
+    ranked = p.num_seqs <= kRankMax;
+    if (ranked) {
+      int rj = 0, nj = 0, lj = 0;
+      bool act = false;
+      if (tid < p.num_seqs) {
+        rj = p.q_indptr[tid];
+        nj = p.q_indptr[tid + 1] - rj;
+        lj = p.seq_lens[tid];
+        act = nj > 1 || (nj == 1 && !p.skip_single);
+      }
+      // stable partition: active requests first
+      const uint64_t bal = __ballot(act);
+      const int below = __popcll(bal & ((1ull << lane) - 1));
+      if (lane == 0) s_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int before = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = s_cnt[w];
+        before += w < wave ? c : 0;
+        n_active += c;
+      }
+      if (tid < p.num_seqs) {
+        const int pos = act ? before + below : n_active + (tid - before - below);
+        s_req[0][pos] = tid;
+        s_req[1][pos] = rj;
+        s_req[2][pos] = nj;
+        s_req[3][pos] = lj;
+      }
+      __syncthreads();
+      if (n_active > 1 && n_active <= 64) {  // uniform
+        if (wave == 0) {
+          int rb = 0, rr = 0, rn = 0, cost = INT_MIN;
+          if (lane < n_active) {
+            rb = s_req[0][lane];
+            rr = s_req[1][lane];
+            rn = s_req[2][lane];
+            cost = s_req[3][lane];
+          }
+          int myrank = 0;  // ties keep the partition order
+          for (int i = 0; i < n_active; ++i) {  // uniform loop
+            const int ci = __builtin_amdgcn_readlane(cost, i);
+            const int rank = __popcll(__ballot(cost > ci)) + __popcll(__ballot(cost == ci) & ((1ull << i) - 1));
+            if (lane == i) myrank = rank;
+          }
+          if (lane < n_active) {
+            s_req[0][myrank] = rb;
+            s_req[1][myrank] = rr;
+            s_req[2][myrank] = rn;
+            s_req[3][myrank] = cost;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- the work-group's items.  Extend: logical item ids are (token block
+  // qb, request rank, KV head g) with qb fastest and heaviest (latest)
+  // first, so consecutive ids of one (request, head) read the same keys.
+  // The ids are split into 8 contiguous ranges, one per XCD (work-group i
+  // runs on XCD i mod 8); the W work-groups of an XCD take its range in
+  // rounds of W, alternating direction, so that a work-group pairs heavy
+  // items with light ones.  A grid of one work-group per item takes one
+  // round.  Shared-prefix pass: one item per work-group.
+  const int xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
+  const int wx = ((int)gridDim.x - xcd + 7) / 8;  // work-groups on this XCD
+  for (int item = 0;; ++item) {
   int g, q_row, vis_lim, k_begin, k_end, min_vis, piece = 0;
   bool qvalid, has_keys;
   const int32_t* pt;
   if constexpr (!PREFIX) {
-    // work-group: token block qb of (request b, KV head g).  The blocks of
-    // one (request, head) are consecutive logical ids, heaviest (latest)
-    // first, then requests, then heads: each XCD runs whole (request, head)
-    // groups, which read the same keys, and a fair mix of requests.  In a
-    // batch of at most 64 requests, the requests go in order of decreasing
-    // key count, so that the longest work-groups start first and the
-    // shortest fill the end.
     const int qblocks = (p.max_q_len + TOK - 1) / TOK;
-    int bid = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int total = qblocks * p.num_kv_heads * p.num_seqs;
+    const int q8 = total / 8, r8 = total % 8;
+    const int nx = q8 + (xcd < r8 ? 1 : 0);
+    const int start = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
+    const int within = item * wx + ((item & 1) ? wx - 1 - kx : kx);
+    if (within >= nx) break;  // uniform
+    int bid = start + within;
     const int qb = qblocks - 1 - (bid % qblocks);
     bid /= qblocks;
-    int b = bid % p.num_seqs;
+    const int rk = bid % p.num_seqs;
     g = bid / p.num_seqs;
-    int r0, n, L;
-    if (p.num_seqs <= 64) {
-      // lane j: request j's row range and cost (its key count; -1 when the
-      // request runs no work-group here); ties keep the request order
-      int cost = INT_MIN, rj = 0, nj = 0, lj = 0;
-      if (lane < p.num_seqs) {
-        rj = p.q_indptr[lane];
-        nj = p.q_indptr[lane + 1] - rj;
-        lj = p.seq_lens[lane];
-        cost = (nj > 1 || (nj == 1 && !p.skip_single)) ? lj : -1;
+    int b, r0, n, L;
+    if (ranked) {
+      if (rk >= n_active) {
+        // the rest of this head's ids are inactive requests too: go on at
+        // the round that reaches the next head's first id
+        const int next = (g + 1) * qblocks * p.num_seqs - start;
+        if (next >= nx) break;
+        item = max(item, next / wx - 1);
+        continue;
       }
-      int sel = b;
-      for (int i = 0; i < p.num_seqs; ++i) {  // uniform loop
-        const int ci = __builtin_amdgcn_readlane(cost, i);
-        const int rank = __popcll(__ballot(cost > ci)) + __popcll(__ballot(cost == ci) & ((1ull << i) - 1));
-        if (rank == b) sel = i;
-      }
-      b = sel;
-      r0 = __builtin_amdgcn_readlane(rj, b);
-      n = __builtin_amdgcn_readlane(nj, b);
-      L = __builtin_amdgcn_readlane(lj, b);
+      b = s_req[0][rk];
+      r0 = s_req[1][rk];
+      n = s_req[2][rk];
+      L = s_req[3][rk];
     } else {
+      b = rk;
       r0 = p.q_indptr[b];
       n = p.q_indptr[b + 1] - r0;
       L = p.seq_lens[b];
     }
     const int i0 = qb * TOK;
-    if (i0 >= n || (n == 1 && p.skip_single)) return;
+    if (i0 >= n || (n == 1 && p.skip_single)) continue;  // uniform
     const int prefix = L - n;
     k_begin = 0;
     k_end = prefix + min(i0 + TOK, n);  // keys this block can see
@@ -160,6 +232,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     pt = p.page_table + (int64_t)b * p.pt_stride;
   } else {
     // work-group: key piece sp of row block rb of (group j, KV head g)
+    if (item > 0) break;
     const int rblocks = (p.max_q_len + TOK - 1) / TOK;
     int bid = blockIdx.x;
     piece = bid % p.num_pieces;
@@ -171,7 +244,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     const int m_begin = p.q_indptr[j];
     const int gsize = p.q_indptr[j + 1] - m_begin;
     const int m0 = rb * TOK;
-    if (m0 >= gsize) return;
+    if (m0 >= gsize) break;
     const int mi = m0 + (row % TOK);
     qvalid = mi < gsize;
     q_row = m_begin + (qvalid ? mi : m0);
@@ -199,7 +272,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
       mx = max(mx, s_red[0][w]);
       mn = min(mn, s_red[1][w]);
     }
-    if (k_begin >= mx) return;  // no row of the block reads this piece (uniform)
+    if (k_begin >= mx) break;  // no row of the block reads this piece (uniform)
     k_end = min(k_begin + p.piece_keys, mx);
     min_vis = mn - 1;
     pt = p.page_table + (int64_t)j * p.pt_stride;
@@ -502,7 +575,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   // ---- normalise and write this lane's row
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
   if constexpr (!PREFIX) {
-    if (!qvalid) return;
+    if (qvalid) {
     const float inv = 1.f / l_tot;
     uint16_t* op = (uint16_t*)p.out + ((int64_t)q_row * p.num_q_heads + (int64_t)g * G + hq) * D;
 #pragma unroll
@@ -515,10 +588,11 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
         w.y = pack2(o[i][4 * q4 + 2] * inv, o[i][4 * q4 + 3] * inv);
         *(uint2*)(op + d) = w;
       }
+    }
   } else {
     // the combine kernel reads this piece for a member only if the member
     // has keys in it
-    if (!has_keys) return;
+    if (has_keys) {
     const float inv = 1.f / l_tot;
     const int64_t wrow = ((int64_t)q_row * p.num_q_heads + (int64_t)g * G + hq) * p.ws_pieces + piece;
     float* op = p.o_part + wrow * D;
@@ -531,15 +605,32 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
                                          o[i][4 * q4 + 2] * inv, o[i][4 * q4 + 3] * inv);
       }
     if (half == 0) p.lse[wrow] = m_ref * sl2 + __log2f(l_tot);
+    }
   }
+  __syncthreads();  // the next item refills the LDS
+  }  // items
 }
 
 template <int D, int G, bool PREFIX>
 hipError_t launch_g(const ExtendArgs& a, hipStream_t stream) {
   constexpr int TOK = Shape<PREFIX>::kRows / G;
   const int64_t blocks_per = (a.max_q_len + TOK - 1) / TOK;
-  const int64_t blocks = blocks_per * a.num_kv_heads * a.num_seqs * (PREFIX ? a.num_pieces : 1);
+  int64_t blocks = blocks_per * a.num_kv_heads * a.num_seqs * (PREFIX ? a.num_pieces : 1);
   if (blocks == 0) return hipSuccess;
+  if (!PREFIX) {
+    // Up to four chip-fulls of items, one work-group per item: the
+    // dispatcher balances them as slots free up.  Beyond that (typically a
+    // batch of mostly single-row requests, whose items are empty), two
+    // work-groups per compute unit (what fits at once, a multiple of the 8
+    // XCDs) each take their share of the items and skip the empty ones
+    // without a launch each.
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t cap = (int64_t)(2 * cus) / 8 * 8;
+    if (cap >= 8 && blocks > 4 * cap) blocks = cap;
+  }
   hipLaunchKernelGGL((mfma_attn_kernel<D, G, PREFIX>), dim3((unsigned)blocks), dim3(Shape<PREFIX>::kThreads), 0,
                      stream, a);
   return hipGetLastError();

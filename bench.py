@@ -37,9 +37,12 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 PROFILE_COUNTERS = {
     "cascade": os.path.join(ROOT, "profiles", "decode_partial_own_keys_qwen3_8b_radix_counters.txt"),
     "plain": os.path.join(ROOT, "profiles", "decode_partial_qwen3_8b_radix_counters.txt"),
+    "extend": os.path.join(ROOT, "profiles", "extend_qwen3_8b_extend_counters.txt"),
 }
-DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_attention_11_amd", "csrc", f)
-                  for f in ("decode.hip", "device.h", "internal.h")]
+_CSRC = os.path.join(ROOT, "paged_kv_attention_11_amd", "csrc")
+DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("decode.hip", "device.h", "internal.h")]
+EXTEND_SOURCES = [os.path.join(_CSRC, f) for f in ("extend.hip", "mfma_tile.h", "device.h", "internal.h")]
+KERNEL_SOURCES = {"cascade": DECODE_SOURCES, "plain": DECODE_SOURCES, "extend": EXTEND_SOURCES}
 
 
 def parse():
@@ -83,7 +86,7 @@ def read_traffic(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != sources_digest(DECODE_SOURCES):
+    if kv.get("source_digest") != sources_digest(KERNEL_SOURCES[path]):
         return None
     try:
         return float(kv["hbm_bytes_per_dispatch"])
@@ -539,8 +542,8 @@ def main():
             "kernel_us": round(ems * 1e3, 2),
             "tokens_per_s": round(int(n.sum()) / (ems * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                         "algorithmic_flops_per_launch": flops},
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": read_traffic("extend"), "algorithmic_flops_per_launch": flops},
         }
         log(f"extend: {ems * 1e3:.1f} us, {tf:.1f} TFLOP/s")
 

@@ -399,7 +399,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = kb + 32 * (ks ^ (ck >> 1));
     const int j = lane & 15, g1 = (lane >> 4) & 1;
-    const int sv = v_swz<D>(j >> 2);  // keys read here are j/4 mod 4
+    const int sv = v_swz<D>(4 * half + (j >> 2));  // the keys read here, mod 8
     const int pl = (4 * half + (j >> 2)) * PPR * 16 + 8 * (j & 1) + 16 * ((2 * g1 + ((j >> 1) & 1)) ^ (sv & 3));
 #pragma unroll
     for (int i = 0; i < DT; ++i) voff[i] = pl + 64 * (i ^ (sv >> 2));

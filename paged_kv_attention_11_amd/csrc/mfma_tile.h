@@ -47,17 +47,20 @@ constexpr int kPageCap = 1024;  // page ids staged in LDS at a time
 // 32 keys read by one MFMA operand fetch hit distinct banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int key) { return key & (ExtCfg<D>::PPR - 1); }
-// V rows: piece p of key k at p ^ v_swz(k).  For D = 128 (four 64-byte
-// blocks per row) the block index is XORed with k mod 4 and the 16-byte
-// chunk with bit 1 of k: the 4 keys x 64 bytes that half a wave reads with
-// one transposing read cover all 256 bytes of the bank space, and any 16
-// lanes cover 128 distinct bytes.  For D = 64, p ^ 2(k mod 4).
+// V rows: piece p of key k at p ^ v_swz(k), an XOR-linear function of the
+// key's low three bits.  For D = 128 (four 64-byte blocks per row) bit 0
+// moves the 64-byte block by one, bit 1 by two and the 16-byte chunk by two,
+// bit 2 the chunk by two; for D = 64, pieces 2, 4 and 2.  Both transposing
+// read patterns that use the layout (extend: lanes over 4 keys x 64 bytes,
+// twice; verify: lanes over 8 keys x 32 bytes) then fall on distinct LDS
+// banks, with 32 banks and with 64 (checked exhaustively on the CPU).
 template <int D>
 __device__ __forceinline__ int v_swz(int key) {
+  const int b2 = 2 * ((key >> 2) & 1);
   if constexpr (ExtCfg<D>::PPR == 16)
-    return 4 * (key & 3) + 2 * ((key >> 1) & 1);
+    return (4 * (key & 3) + 2 * ((key >> 1) & 1)) ^ b2;
   else
-    return (2 * (key & 3)) & (ExtCfg<D>::PPR - 1);
+    return (2 * (key & 3)) ^ b2;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {

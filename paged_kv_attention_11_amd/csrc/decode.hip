@@ -109,6 +109,7 @@ struct DecodeOcc {
   // compiler's register report so that no instantiation spills to scratch
   // memory inside the key loop.
   static constexpr int kWaves = (BF16 && G == 8)               ? 2
+                                : (BF16 && D == 128 && G == 3) ? 4
                                 : (BF16 && D == 64 && G == 7)  ? 3
                                 : (D == 64 && G == 5)          ? 4
                                 : (!BF16 && D == 64 && G == 8) ? 3
@@ -120,7 +121,22 @@ struct DecodeOcc {
 #define PA_DECODE_WAVES(B, D, G) (DecodeOcc<B, D, G>::kWaves)
 #endif
 
-template <bool BF16, int D, int G>
+typedef uint32_t u32x4_nt_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load; NT marks it nontemporal (streamed past the caches).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const void* ptr) {
+  if constexpr (NT)
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_nt_t*)ptr));
+  else
+    return *(const uint4*)ptr;
+}
+
+// NT: the keys are read once per step and nowhere else (each request's own
+// keys in the cascade), so they are loaded nontemporally and leave the
+// caches to the data that is read again (the groups' shared pages, the
+// queries, the partials).
+template <bool BF16, int D, int G, bool NT>
 __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_partial_kernel(
     const DecodeArgs p) {
   using C = DecodeCfg<BF16, D, G>;
@@ -227,11 +243,11 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
     const int ik = min(ib + tq, n_tok - 1);
     const T* kp = kbase + (int64_t)s_slot[ik] * row_stride;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) tl.k[j] = *(const uint4*)(kp + (c + 4 * j) * EPC);
+    for (int j = 0; j < NK; ++j) tl.k[j] = load16<NT>(kp + (c + 4 * j) * EPC);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int iv = min(ib + j * RPI + vr, n_tok - 1);
-      tl.v[j] = *(const uint4*)(vbase + (int64_t)s_slot[iv] * row_stride + vc * EPC);
+      tl.v[j] = load16<NT>(vbase + (int64_t)s_slot[iv] * row_stride + vc * EPC);
     }
   };
 
@@ -476,7 +492,15 @@ template <bool BF16, int D, int G>
 hipError_t launch_partial_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.num_seqs * a.num_kv_heads * a.max_splits;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_partial_kernel<BF16, D, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
+  // the cascade's own-keys pass (bf16, the group sizes it supports)
+  if constexpr (BF16 && (G == 1 || G == 2 || G == 4 || G == 8)) {
+    if (a.key_begin) {
+      hipLaunchKernelGGL((decode_partial_kernel<BF16, D, G, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_partial_kernel<BF16, D, G, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
 }

@@ -143,9 +143,30 @@ def bench_decode_configs(pa, W, torch, np, stream, iters):
         pa.kv_store(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slot_mapping)
         o = torch.empty_like(d.q)
         ws = pa.decode_workspace(d.q, d.k_pool, wl.max_seq_len)
-        ms = _time(torch, stream, lambda: pa.decode(d.q, d.k_pool, d.v_pool, d.page_table, d.seq_lens, wl.max_seq_len,
-                                                    wl.scale, o, ws), iters)
-        out[name] = {"us": round(ms * 1e3, 2), "GBps_unique": round(wl.kv_bytes_unique() / (ms * 1e-3) / 1e9, 1),
+        def f():
+            pa.decode(d.q, d.k_pool, d.v_pool, d.page_table, d.seq_lens, wl.max_seq_len, wl.scale, o, ws)
+
+        ms = _time(torch, stream, f, iters)
+        # The same calls captured back to back into one HIP graph: at these
+        # sizes a call from Python costs more host time than the GPU spends,
+        # so the replay shows the GPU-side time per call.
+        per_graph = 20
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                f()
+        torch.cuda.synchronize()
+        gms = _time(torch, stream, graph.replay, max(3, iters // per_graph)) / per_graph
+        del graph
+        out[name] = {"us": round(ms * 1e3, 2), "graph_us": round(gms * 1e3, 2),
+                     "GBps_unique": round(wl.kv_bytes_unique() / (ms * 1e-3) / 1e9, 1),
+                     "GBps_unique_graph": round(wl.kv_bytes_unique() / (gms * 1e-3) / 1e9, 1),
                      "tokens_per_s": round(wl.num_seqs / (ms * 1e-3), 1), "dtype": wl.dtype,
                      "description": W.DESCRIPTIONS[name]}
         del d, ws
@@ -550,7 +571,7 @@ def main():
     # ---------------- the other decode configurations (plain decode, one call)
     if not args.no_extend:
         result["decode_configs"] = bench_decode_configs(pa, W, torch, np, stream, max(10, args.steps))
-        log("decode configs: " + ", ".join(f"{k} {v['us']} us ({v['GBps_unique']} GB/s)"
+        log("decode configs: " + ", ".join(f"{k} {v['us']} us, {v['graph_us']} us in a graph ({v['GBps_unique']} GB/s)"
                                            for k, v in result["decode_configs"].items()))
 
     # ---------------- fused rotary embedding + store (the step before attention)

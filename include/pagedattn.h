@@ -177,7 +177,10 @@ int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t m
  * (0 = the automatic plan); 0 on invalid sizes.  Layout:
  * fp32 partial outputs [num_seqs, num_q_heads, S, head_dim] followed (at a
  * 256-byte boundary) by fp32 log2-sum-exp values [num_seqs, num_q_heads, S],
- * S = ceil(max_seq_len / split_tokens).
+ * S = ceil(max_seq_len / split_tokens), and, when S > 1, (at a 256-byte
+ * boundary) the order in which the partial kernel takes the pieces, int32
+ * [S * num_seqs, 4], written by a one-work-group kernel that pa_decode_partial
+ * launches first on large batches.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len, int32_t split_tokens);
@@ -279,7 +282,8 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
  *                       values [num_seqs, num_q_heads, NP + S], where
  *                       NP = ceil(max_shared_len / prefix_piece_keys) pieces
  *                       of kernel 1 come first and S = ceil(max_seq_len /
- *                       split_tokens) pieces of kernel 2 follow.
+ *                       split_tokens) pieces of kernel 2 follow; then, when
+ *                       S > 1, the work order of kernel 2 as for pa_decode.
  * bf16 pools only, head_dim 128 or 64, group size (num_q_heads /
  * num_kv_heads) 1, 2, 4 or 8.  A request with seq_len 0 gets a zero row.
  */

@@ -73,11 +73,24 @@ int32_t resolve_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_hea
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Work order of the decode partial kernel (a plan kernel lists the pieces
+// that exist, longest first).  The plan kernel is one more launch of a few
+// microseconds, so it is used only on grids of at least kPlanMinBlocks
+// work-groups; the workspace always has room for it when there is more than
+// one piece per request.
+constexpr int64_t kPlanMinBlocks = 8192;
+
+size_t plan_bytes(int32_t num_seqs, int64_t S) { return S > 1 ? align256((size_t)num_seqs * S * 16) : 0; }
+
+bool use_plan(int32_t num_seqs, int32_t num_kv_heads, int64_t S) {
+  return S > 1 && (int64_t)num_seqs * num_kv_heads * S >= kPlanMinBlocks;
+}
+
 size_t workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
                        int32_t split) {
   const int64_t S = (max_seq_len + split - 1) / split;
   const size_t rows = (size_t)num_seqs * num_q_heads * S;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float)) + plan_bytes(num_seqs, S);
 }
 
 // Shared validation of the three decode calls; fills `a` on success.
@@ -130,6 +143,10 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   a.group_piece_keys = 1;
   a.bf16 = pool->dtype == PA_BF16;
   a.scale_log2 = scale * kLog2e;
+  a.plan = workspace && use_plan(num_seqs, pool->num_kv_heads, S)
+               ? (int4*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float)) +
+                         align256(rows * sizeof(float)))
+               : nullptr;
   return PA_OK;
 }
 
@@ -169,7 +186,7 @@ size_t cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t he
   const int64_t S = (max_seq_len + split - 1) / split;
   const int64_t NP = (max_shared_len + piece_keys - 1) / piece_keys;
   const size_t rows = (size_t)num_seqs * num_q_heads * (S + NP);
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float)) + plan_bytes(num_seqs, S);
 }
 
 }  // namespace
@@ -456,6 +473,9 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   a.group_piece_keys = pk;
   a.bf16 = 1;
   a.scale_log2 = scale * kLog2e;
+  a.plan = use_plan(num_seqs, pool->num_kv_heads, S)
+               ? (int4*)((char*)lse + align256(rows * sizeof(float)))
+               : nullptr;
   if (stages & kStageSuffix) {
     st = hip_status(pa::launch_decode_partial(a, hs));
     if (st != PA_OK) return st;

@@ -88,6 +88,10 @@ struct DecodeArgs {
   int32_t group_piece_keys;
   int32_t bf16;
   float scale_log2;  // softmax scale * log2(e)
+  // [max_splits * num_seqs] work order of the partial kernel, written by a
+  // plan kernel launched before it; null: every (piece, request, head) of
+  // the grid in piece-major order
+  int4* plan;
 };
 
 // Matrix-core attention tiles: the extend call, and the shared-prefix pass of

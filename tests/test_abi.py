@@ -117,8 +117,12 @@ def test_decode_workspace_size_matches_layout():
     assert lib.pa_decode_split_tokens(256, 8, 8192) == 1024
     S = 8
     rows = 256 * 32 * S
-    expect = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    a256 = lambda x: (x + 255) // 256 * 256
+    # partials, log-sum-exps, then the work order (int32 x 4 per piece and request)
+    expect = a256(rows * 128 * 4) + a256(rows * 4) + a256(S * 256 * 16)
     assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 0) == expect
+    # one piece per request: no work order
+    assert lib.pa_decode_workspace_bytes(4, 2, 1, 64, 64, 0) == a256(4 * 2 * 64 * 4) + a256(4 * 2 * 4)
     assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 100) == 0  # invalid split
     assert lib.pa_decode_workspace_bytes(-1, 32, 8, 128, 8192, 0) == 0
 
@@ -198,7 +202,8 @@ def test_cascade_plan_and_workspace():
     B, Hq, D, L, msh = 256, 32, 128, 8192, 1024
     S, NP = 8, 2
     rows = B * Hq * (S + NP)
-    expect = ((rows * D * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    a256 = lambda x: (x + 255) // 256 * 256
+    expect = a256(rows * D * 4) + a256(rows * 4) + a256(S * B * 16)
     assert lib.pa_decode_cascade_workspace_bytes(B, Hq, 8, D, L, 0, 16, 16, msh, 0) == expect
     assert lib.pa_decode_cascade_workspace_bytes(B, Hq, 8, D, L, 0, 16, 16, msh, 96) == 0
     assert lib.pa_decode_cascade_workspace_bytes(B, 30, 8, D, L, 0, 16, 16, msh, 0) == 0

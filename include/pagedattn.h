@@ -165,9 +165,9 @@ pa_status pa_rope_kv_store(const pa_kv_pool* pool, const void* q, int32_t num_q_
  * pieces of split_tokens keys; each (request, KV head, piece) is one unit of
  * work, and a second kernel merges the pieces by log-sum-exp weights.
  * pa_decode_split_tokens returns the piece length the library chooses from
- * the host-side sizes alone (a multiple of 64, at most 1024).  Every decode
+ * the host-side sizes alone (a multiple of 64, at most 2048).  Every decode
  * call takes a split_tokens argument: 0 means "this automatic choice", any
- * other value must be a multiple of 64 in [64, 1024].  The result depends on
+ * other value must be a multiple of 64 in [64, 2048].  The result depends on
  * the split only through floating-point rounding.
  */
 int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len);
@@ -336,8 +336,9 @@ pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32
  * pa_verify: the result of pa_extend (same arguments and semantics) for
  * requests whose chunks are short, as in the verification of drafted tokens:
  * max_q_len * (num_q_heads / num_kv_heads) <= 32.  The keys of each request
- * are split into pieces of split_tokens keys (0 = pa_decode_split_tokens'
- * choice; else a multiple of 64 in [64, 1024]) handled by separate
+ * are split into pieces of split_tokens keys (0 = the automatic choice, as
+ * pa_decode_split_tokens' but at most 1024; else a multiple of 64 in
+ * [64, 1024]) handled by separate
  * work-groups, each reading a K/V tile once for all rows of the chunk and all
  * query heads of a KV head; a second kernel merges the pieces.
  *   workspace: pa_verify_workspace_bytes(...) bytes, 256-byte aligned

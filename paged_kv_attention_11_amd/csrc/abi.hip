@@ -15,16 +15,18 @@ using pa::kSplitQuantum;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Automatic split plan: the longest piece (a multiple of 64, at most 1024)
-// that still gives about kTargetUnits work-groups, i.e. two rounds of a full
-// chip at the decode kernel's occupancy; when no piece length gets there the
-// batch cannot fill the chip anyway, and pieces of 256 keys (fewer
-// work-groups, less to merge) are fastest.  Measured on one MI355X:
-// Qwen3-0.6B-shaped decode (64 requests x 8 KV heads, <= 2048 keys) 53 us at
-// 256 against 58 us at 512; Qwen2.5-0.5B-shaped (32 x 2, <= 640 keys) 16.3 us
-// at 256 against 18.7 us at 64; Qwen3-8B-shaped (256 x 8, <= 8192) 1024.
+// Automatic split plan: the longest piece (a multiple of 64, at most
+// kMaxSplitTokens for decode, kVerifyMaxSplit for verify) that still gives
+// about kTargetUnits work-groups, i.e. two rounds of a full chip at the
+// decode kernel's occupancy; when no piece length gets there the batch
+// cannot fill the chip anyway, and pieces of 256 keys (fewer work-groups,
+// less to merge) are fastest.  Measured on one MI355X: Qwen3-0.6B-shaped
+// decode (64 requests x 8 KV heads, <= 2048 keys) 53 us at 256 against 58 us
+// at 512; Qwen2.5-0.5B-shaped (32 x 2, <= 640 keys) 16.3 us at 256 against
+// 18.7 us at 64; Qwen3-8B-shaped radix batch (256 x 8, <= 8192 keys, in the
+// work order below) each request's own keys 403 us at 2048, 406 at 1536,
+// 412 at 1024 and 432 at 512.
 constexpr int64_t kTargetUnits = 4096;
-constexpr int kAutoMaxSplit = 1024;
 constexpr int kSmallBatchSplit = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -52,23 +54,23 @@ pa_status check_pool(const pa_kv_pool* pool) {
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-int32_t resolve_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len);
-
-int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t max_split) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return kSplitQuantum;
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  for (int64_t split = kAutoMaxSplit; split >= kSplitQuantum; split -= kSplitQuantum)
+  for (int64_t split = max_split; split >= kSplitQuantum; split -= kSplitQuantum)
     if (units * ((max_seq_len + split - 1) / split) >= kTargetUnits) return (int32_t)split;
   // too small to fill the chip: 256-key pieces, or one piece if shorter
   const int64_t one = (max_seq_len + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
   return (int32_t)(one < kSmallBatchSplit ? one : kSmallBatchSplit);
 }
 
-bool valid_split(int32_t s) { return s >= kSplitQuantum && s <= kMaxSplitTokens && s % kSplitQuantum == 0; }
-
-int32_t resolve_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
-  if (split_tokens == 0) return auto_split(num_seqs, num_kv_heads, max_seq_len);
-  return valid_split(split_tokens) ? split_tokens : -1;
+// The split of a call: split_tokens if valid (a multiple of 64 in
+// [64, max_split]), the automatic choice for 0, -1 otherwise.
+int32_t resolve_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                      int32_t max_split = kMaxSplitTokens) {
+  if (split_tokens == 0) return auto_split(num_seqs, num_kv_heads, max_seq_len, max_split);
+  const bool ok = split_tokens >= kSplitQuantum && split_tokens <= max_split && split_tokens % kSplitQuantum == 0;
+  return ok ? split_tokens : -1;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -78,7 +80,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // microseconds, so it is used only on grids of at least kPlanMinBlocks
 // work-groups; the workspace always has room for it when there is more than
 // one piece per request.
-constexpr int64_t kPlanMinBlocks = 8192;
+constexpr int64_t kPlanMinBlocks = 6144;
 
 size_t plan_bytes(int32_t num_seqs, int64_t S) { return S > 1 ? align256((size_t)num_seqs * S * 16) : 0; }
 
@@ -148,6 +150,27 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
                          align256(rows * sizeof(float)))
                : nullptr;
   return PA_OK;
+}
+
+// The work order's inputs for the partial kernel described by `a`.
+pa::PlanArgs plan_args(const pa::DecodeArgs& a) {
+  pa::PlanArgs p;
+  p.plan = a.plan;
+  p.seq_lens = a.seq_lens;
+  p.key_begin = a.key_begin;
+  p.q_indptr = a.q_indptr;
+  p.num_seqs = a.num_seqs;
+  p.split_tokens = a.split_tokens;
+  p.max_splits = a.max_splits;
+  p.always_partial = a.always_partial;
+  return p;
+}
+
+// The partial kernel, after its work order when it has one.
+pa_status enqueue_partial(const pa::DecodeArgs& a, hipStream_t stream) {
+  pa_status st = hip_status(pa::launch_decode_plan(plan_args(a), stream));
+  if (st != PA_OK) return st;
+  return hip_status(pa::launch_decode_partial(a, stream));
 }
 
 // Shared-prefix pass of the cascade decode: keys per piece.  The plan aims
@@ -263,7 +286,7 @@ pa_status pa_rope_kv_store(const pa_kv_pool* pool, const void* q, int32_t num_q_
 }
 
 int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
-  return auto_split(num_seqs, num_kv_heads, max_seq_len);
+  return auto_split(num_seqs, num_kv_heads, max_seq_len, kMaxSplitTokens);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -283,7 +306,7 @@ pa_status pa_decode_partial(const pa_kv_pool* pool, const void* q, int32_t num_q
   pa_status st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs,
                                 max_seq_len, scale, split_tokens, out, workspace, workspace_bytes_, a);
   if (st != PA_OK || num_seqs == 0) return st;
-  return hip_status(pa::launch_decode_partial(a, (hipStream_t)stream));
+  return enqueue_partial(a, (hipStream_t)stream);
 }
 
 pa_status pa_decode_combine(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
@@ -305,7 +328,7 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   pa_status st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs,
                                 max_seq_len, scale, split_tokens, out, workspace, workspace_bytes_, a);
   if (st != PA_OK || num_seqs == 0) return st;
-  st = hip_status(pa::launch_decode_partial(a, (hipStream_t)stream));
+  st = enqueue_partial(a, (hipStream_t)stream);
   if (st != PA_OK) return st;
   // one piece per request: the partial kernel wrote every row (zero rows too)
   if (a.max_splits <= 1) return PA_OK;
@@ -420,34 +443,7 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   float* lse = (float*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float)));
   const hipStream_t hs = (hipStream_t)stream;
 
-  // pass 1: each group's shared pages, all members' queries in one tile
-  if (prefix_pass && (stages & kStagePrefix)) {
-    pa::ExtendArgs e = {};
-    e.k_pool = pool->k_pool;
-    e.v_pool = pool->v_pool;
-    e.q = q;
-    e.q_indptr = group_starts;
-    e.page_table = prefix_page_table;
-    e.seq_lens = shared_lens;
-    e.o_part = o_part;
-    e.lse = lse;
-    e.pt_stride = prefix_pt_stride;
-    e.num_seqs = num_groups;
-    e.num_q_heads = num_q_heads;
-    e.num_kv_heads = pool->num_kv_heads;
-    e.head_dim = pool->head_dim;
-    e.log2_page = ilog2(pool->page_size);
-    e.max_q_len = max_group_size;
-    e.max_keys = max_shared_len;
-    e.piece_keys = pk;
-    e.num_pieces = (int32_t)NP;
-    e.ws_pieces = (int32_t)(S + NP);
-    e.scale_log2 = scale * kLog2e;
-    st = hip_status(pa::launch_prefix(e, hs));
-    if (st != PA_OK) return st;
-  }
-
-  // pass 2: each request's own keys [shared_len, seq_len); pass 3: merge
+  // pass 2 (each request's own keys [shared_len, seq_len)) and pass 3 (the merge)
   pa::DecodeArgs a = {};
   a.k_pool = pool->k_pool;
   a.v_pool = pool->v_pool;
@@ -476,6 +472,38 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   a.plan = use_plan(num_seqs, pool->num_kv_heads, S)
                ? (int4*)((char*)lse + align256(rows * sizeof(float)))
                : nullptr;
+  // pass 1: each group's shared pages, all members' queries in one tile, and
+  // the work order of pass 2 (when it has one)
+  if (prefix_pass && (stages & kStagePrefix)) {
+    pa::ExtendArgs e = {};
+    e.k_pool = pool->k_pool;
+    e.v_pool = pool->v_pool;
+    e.q = q;
+    e.q_indptr = group_starts;
+    e.page_table = prefix_page_table;
+    e.seq_lens = shared_lens;
+    e.o_part = o_part;
+    e.lse = lse;
+    e.pt_stride = prefix_pt_stride;
+    e.num_seqs = num_groups;
+    e.num_q_heads = num_q_heads;
+    e.num_kv_heads = pool->num_kv_heads;
+    e.head_dim = pool->head_dim;
+    e.log2_page = ilog2(pool->page_size);
+    e.max_q_len = max_group_size;
+    e.max_keys = max_shared_len;
+    e.piece_keys = pk;
+    e.num_pieces = (int32_t)NP;
+    e.ws_pieces = (int32_t)(S + NP);
+    e.scale_log2 = scale * kLog2e;
+    e.plan = plan_args(a);  // its extra work-group writes pass 2's work order
+    st = hip_status(pa::launch_prefix(e, hs));
+    if (st != PA_OK) return st;
+  } else if (stages & kStagePrefix) {
+    st = hip_status(pa::launch_decode_plan(plan_args(a), hs));
+    if (st != PA_OK) return st;
+  }
+
   if (stages & kStageSuffix) {
     st = hip_status(pa::launch_decode_partial(a, hs));
     if (st != PA_OK) return st;
@@ -528,7 +556,7 @@ pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_h
   a.always_partial = 0;
   const hipStream_t hs = (hipStream_t)stream;
   // requests with one new row: split-K decode; the others: matrix-core tiles
-  st = hip_status(pa::launch_decode_partial(a, hs));
+  st = enqueue_partial(a, hs);
   if (st != PA_OK) return st;
   if (max_q_len > 1) {
     pa::ExtendArgs e = {};
@@ -558,7 +586,7 @@ size_t pa_verify_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t nu
                                  int32_t head_dim, int32_t max_seq_len, int32_t split_tokens) {
   if (num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
     return 0;
-  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
+  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len, pa::kVerifyMaxSplit);
   if (split < 0) return 0;
   const int64_t S = (max_seq_len + split - 1) / split;
   const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * (S > 1 ? S : 0);
@@ -580,7 +608,7 @@ pa_status pa_verify(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   if ((int64_t)max_q_len * G > 32) return PA_ERR_UNSUPPORTED;  // rows of one matrix-core tile pair
   if (max_q_len > max_seq_len) return PA_ERR_SHAPE;
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
-  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
+  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len, pa::kVerifyMaxSplit);
   if (split < 0) return PA_ERR_SHAPE;
   const int64_t S = (max_seq_len + split - 1) / split;
   if ((int64_t)num_seqs * pool->num_kv_heads * S > (int64_t)INT_MAX) return PA_ERR_SHAPE;

@@ -32,15 +32,14 @@
 //    denominator carry the same reference.
 //  * Key slots of the piece (page_table[t / P] * P + t % P) are computed once
 //    per work-group into LDS.
-//  * Work order.  On large batches a one-work-group plan kernel first lists
-//    the pieces that exist, longest first, so the partial kernel's grid
-//    holds no work-groups for pieces past a request's end before the last
-//    real one, and the short pieces run at the end, where they fill the gaps
-//    that the long ones leave.
+//  * Work order.  On large batches one work-group first lists the pieces
+//    that exist, longest first (plan.h), and the partial kernel's
+//    work-groups take them in that order.
 #include <type_traits>
 
 #include "device.h"
 #include "internal.h"
+#include "plan.h"
 
 namespace pa {
 
@@ -143,140 +142,11 @@ __device__ __forceinline__ uint4 load16(const void* ptr) {
     return *(const uint4*)ptr;
 }
 
-// ---- work order of the partial kernel --------------------------------------
-// Entry i of the plan is the piece that work-groups i * H_kv .. i * H_kv +
-// H_kv - 1 take: {request, piece | kPlanSingle when it is the request's only
-// piece and finishes the output, first key, keys}; keys = 0 marks a request
-// with no keys that gets a zero row; request -1 marks no work.  Order: every
-// full piece (split_tokens keys) in request order, then the shorter last
-// pieces by decreasing key count in classes of 64 keys (request order within
-// a class), then the zero rows, then the empty entries up to max_splits x
-// num_seqs.  Read-only probes of this access pattern on the Qwen3-8B-shaped
-// radix batch (log-uniform lengths) moved 5.44 TB/s with the pieces in grid
-// order among the empty work-groups, 5.61 TB/s with only the existing pieces
-// in the same order, and 5.88 TB/s with the full pieces first.
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kPlanSingle = 1 << 30;
-constexpr int kPlanClasses = kMaxSplitTokens / kSplitQuantum + 2;  // none, 16 key-count classes, zero row
-constexpr int kPlanZero = kPlanClasses - 1;
 
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeArgs p) {
-  __shared__ int s_wfull[kPlanWaves];
-  __shared__ int s_wcnt[kPlanWaves][kPlanClasses];
-  __shared__ int s_base[kPlanClasses];  // next free entry of each class
-  __shared__ int s_full;                // next free entry of the full pieces
-  __shared__ int s_total;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = p.split_tokens, S = p.max_splits, B = p.num_seqs;
-  const uint64_t below = (1ull << lane) - 1;
-
-  auto incl_scan = [&](int x) {  // inclusive prefix sum over the wave
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int y = __shfl_up(x, m, 64);
-      if (lane >= m) x += y;
-    }
-    return x;
-  };
-
-  // request b: full pieces, class of its last piece (0: none), first key
-  struct Req {
-    int nfull, cls, k0, nlast;
-    bool single;
-  };
-  auto info = [&](int b) {
-    Req r = {0, 0, 0, 0, false};
-    if (b >= B) return r;
-    if (p.q_indptr && p.q_indptr[b + 1] - p.q_indptr[b] != 1) return r;  // not a decode request
-    const int L = p.seq_lens[b];
-    r.k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
-    const int own = max(L - r.k0, 0);
-    const int ns = min(own / split + (own % split != 0 ? 1 : 0), S);
-    r.nfull = min(own / split, ns);
-    r.single = ns == 1 && !p.always_partial;
-    if (ns > r.nfull) {
-      r.nlast = own - r.nfull * split;
-      r.cls = (r.nlast + kSplitQuantum - 1) / kSplitQuantum;
-    } else if (L <= 0 && !p.key_begin && !p.always_partial) {
-      r.cls = kPlanZero;
-    }
-    return r;
-  };
-
-  // pass 1: how many entries of each kind
-  if (tid < kPlanClasses) s_base[tid] = 0;
-  if (tid == 0) s_full = 0;
-  __syncthreads();
-  for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
-    const Req r = info(b0 + tid);
-    const int nf = incl_scan(r.nfull);
-    if (lane == 63 && nf) atomicAdd(&s_full, nf);
-    for (int c = 1; c < kPlanClasses; ++c) {
-      const int n = __popcll(__ballot(r.cls == c));
-      if (lane == 0 && n) atomicAdd(&s_base[c], n);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {  // classes in decreasing key count after the full pieces; zero rows last
-    int next = s_full;
-    for (int c = kPlanClasses - 2; c >= 1; --c) {
-      const int n = s_base[c];
-      s_base[c] = next;
-      next += n;
-    }
-    const int nz = s_base[kPlanZero];
-    s_base[kPlanZero] = next;
-    s_total = next + nz;
-    s_full = 0;
-  }
-  __syncthreads();
-
-  // pass 2: write the entries
-  int4* plan = p.plan;
-  for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
-    const int b = b0 + tid;
-    const Req r = info(b);
-    // full pieces: exclusive prefix over the work-group
-    const int incl = incl_scan(r.nfull);
-    if (lane == 63) s_wfull[wave] = incl;
-    int rank = 0;
-    for (int c = 1; c < kPlanClasses; ++c) {
-      const uint64_t bal = __ballot(r.cls == c);
-      if (r.cls == c) rank = __popcll(bal & below);
-      if (lane == 0) s_wcnt[wave][c] = __popcll(bal);
-    }
-    __syncthreads();
-    int fpos = s_full + incl - r.nfull;
-    int cpos = r.cls ? s_base[r.cls] + rank : 0;
-    for (int w = 0; w < wave; ++w) {
-      fpos += s_wfull[w];
-      if (r.cls) cpos += s_wcnt[w][r.cls];
-    }
-    const int flag = r.single ? kPlanSingle : 0;
-    for (int s = 0; s < r.nfull; ++s) plan[fpos + s] = make_int4(b, s | flag, r.k0 + s * split, split);
-    if (r.cls == kPlanZero) {
-      plan[cpos] = make_int4(b, 0, 0, 0);
-    } else if (r.cls) {
-      plan[cpos] = make_int4(b, r.nfull | flag, r.k0 + r.nfull * split, r.nlast);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int n = 0;
-      for (int w = 0; w < kPlanWaves; ++w) n += s_wfull[w];
-      s_full += n;
-    }
-    if (tid > 0 && tid < kPlanClasses) {
-      int n = 0;
-      for (int w = 0; w < kPlanWaves; ++w) n += s_wcnt[w][tid];
-      s_base[tid] += n;
-    }
-    __syncthreads();
-  }
-  // the rest: no work
-  const int n = S * B;
-  for (int i = s_total + tid; i < n; i += kPlanThreads) plan[i] = make_int4(-1, 0, 0, 0);
+// The work order of the partial kernel (plan.h), by one work-group.
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const PlanArgs p) {
+  build_decode_plan<kPlanThreads>(p);
 }
 
 // NT: the keys are read once per step and nowhere else (each request's own
@@ -315,41 +185,44 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
     const int i = blockIdx.x / p.num_kv_heads;
     g = blockIdx.x - i * p.num_kv_heads;
     const int4 e = p.plan[i];
-    if (e.x < 0) return;  // uniform over the work-group
     b = e.x;
     s = e.y & (kPlanSingle - 1);
     single = (e.y & kPlanSingle) != 0;
     t_begin = e.z;
     n_tok = e.w;
-    qrow = p.q_indptr ? p.q_indptr[b] : b;
+    // no work, or an entry this batch cannot have (an order written for
+    // another batch): nothing is read or written.  The key range is checked
+    // against the request's length after the slots are staged.
+    if (b < 0 || b >= p.num_seqs || s >= p.max_splits || n_tok > p.split_tokens || t_begin < 0 ||
+        (int64_t)t_begin + n_tok > ((int64_t)p.pt_stride << p.log2_page))
+      return;  // uniform over the work-group
   } else {
     const int units = p.num_seqs * p.num_kv_heads;
     s = blockIdx.x / units;
     const int bg = blockIdx.x - s * units;
     g = bg % p.num_kv_heads;
     b = bg / p.num_kv_heads;
-    // Mixed batch: only requests with one new row, whose query and output
-    // row is q_indptr[b].
-    qrow = b;
-    if (p.q_indptr) {
-      qrow = p.q_indptr[b];
-      if (p.q_indptr[b + 1] - qrow != 1) return;  // uniform over the work-group
-    }
-    // This request's key range is [k0, L); piece s covers split_tokens of it.
-    const int L = p.seq_lens[b];
-    const int k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
+  }
+  // Mixed batch: only requests with one new row, whose query and output row
+  // is q_indptr[b].
+  qrow = b;
+  if (p.q_indptr) {
+    qrow = p.q_indptr[b];
+    if (p.q_indptr[b + 1] - qrow != 1) return;  // uniform over the work-group
+  }
+  // This request's key range is [k0, L)
+  const int L = p.seq_lens[b];
+  const int k0 = p.key_begin ? max(p.key_begin[b], 0) : 0;
+  const bool zero_row = s == 0 && L <= 0 && !p.key_begin && !p.always_partial;
+  if (!p.plan) {  // piece s covers split_tokens keys of the range
     t_begin = k0 + s * p.split_tokens;
-    if (t_begin >= L) {  // uniform over the work-group
-      // a request with no keys gets zero rows here when it has no pieces to
-      // merge later (plain decode)
-      if (!(s == 0 && L <= 0 && !p.key_begin && !p.always_partial)) return;
-      n_tok = 0;
-    } else {
-      n_tok = min(L - t_begin, p.split_tokens);
-    }
+    n_tok = t_begin < L ? min(L - t_begin, p.split_tokens) : 0;
     single = (L - k0 + p.split_tokens - 1) / p.split_tokens == 1 && !p.always_partial;
   }
   if (n_tok <= 0) {
+    // a request with no keys gets zero rows here when it has no pieces to
+    // merge later (plain decode)
+    if (!zero_row) return;  // uniform over the work-group
     const int64_t orow0 = (int64_t)qrow * p.num_q_heads + (int64_t)g * G;
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
       if constexpr (BF16)
@@ -398,6 +271,7 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   }
 
   __syncthreads();  // s_slot and s_q ready
+  if (t_begin < k0 || (int64_t)t_begin + n_tok > L) return;  // (work order only) uniform over the work-group
 
   // Loads are issued unconditionally: a key index past the piece is clamped to
   // the piece's last key (a real row, so no NaN can enter; its weight is 0).
@@ -693,12 +567,13 @@ hipError_t launch_partial_d(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_decode_plan(const PlanArgs& p, hipStream_t stream) {
+  if (!p.plan || p.num_seqs <= 0 || p.max_splits <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
-  if (a.plan && a.num_seqs > 0 && a.max_splits > 0) {
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (a.bf16) {
     if (a.head_dim == 128) return launch_partial_d<true, 128>(a, stream);
     if (a.head_dim == 64) return launch_partial_d<true, 64>(a, stream);

@@ -14,6 +14,8 @@
 // cascade decode: its rows are the members of a request group times their
 // query heads, its keys the group's shared pages, and it writes split-softmax
 // partials that the decode combine kernel merges with each member's own keys.
+// On large batches one more work-group of that pass writes the work order of
+// the decode kernel that takes the own keys next (plan.h).
 //
 // Design (FlashAttention-2 style tiling written for the CDNA4 matrix core):
 //  * Work-group = 4 waves = 128 query rows = (128 / G) tokens (or group
@@ -43,6 +45,7 @@
 #include "device.h"
 #include "mfma_tile.h"
 #include "internal.h"
+#include "plan.h"
 
 namespace pa {
 
@@ -94,6 +97,15 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   __shared__ uint4 s_v[4][32 * PPR];
   __shared__ int32_t s_pages[kPageCap];
   __shared__ int32_t s_red[2][kWaves];
+
+  if constexpr (PREFIX) {
+    // the extra work-group: the work order of the decode partial kernel
+    // that takes each request's own keys next
+    if (p.plan.plan && blockIdx.x == gridDim.x - 1) {
+      build_decode_plan<SH::kThreads>(p.plan);
+      return;
+    }
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -631,6 +643,7 @@ hipError_t launch_g(const ExtendArgs& a, hipStream_t stream) {
     const int64_t cap = (int64_t)(2 * cus) / 8 * 8;
     if (cap >= 8 && blocks > 4 * cap) blocks = cap;
   }
+  if (PREFIX && a.plan.plan) ++blocks;  // the work-group that writes the decode work order
   hipLaunchKernelGGL((mfma_attn_kernel<D, G, PREFIX>), dim3((unsigned)blocks), dim3(Shape<PREFIX>::kThreads), 0,
                      stream, a);
   return hipGetLastError();

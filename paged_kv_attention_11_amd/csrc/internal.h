@@ -12,7 +12,8 @@ namespace pa {
 constexpr int kDecodeWaves = 4;           // waves per decode work-group
 constexpr int kDecodeTokPerIter = 16;     // keys one wave handles per iteration
 constexpr int kSplitQuantum = kDecodeWaves * kDecodeTokPerIter;  // 64
-constexpr int kMaxSplitTokens = 1024;     // LDS slot staging bound
+constexpr int kMaxSplitTokens = 2048;     // decode: LDS slot staging bound
+constexpr int kVerifyMaxSplit = 1024;     // verify: page ids of a piece staged in LDS
 constexpr int kMaxGroup = 8;              // query heads per KV head (decode)
 
 struct StoreArgs {
@@ -59,6 +60,18 @@ struct GatherArgs {
   int32_t row_chunks;
 };
 
+// Inputs of the decode partial kernel's work order (plan.h).
+struct PlanArgs {
+  int4* plan;                // [max_splits * num_seqs] entries written; null: no order
+  const int32_t* seq_lens;   // [B]
+  const int32_t* key_begin;  // [B] first key of each request's range, or null (0)
+  const int32_t* q_indptr;   // [B+1] mixed batches (only one-row requests get pieces), or null
+  int32_t num_seqs;
+  int32_t split_tokens;
+  int32_t max_splits;
+  int32_t always_partial;
+};
+
 struct DecodeArgs {
   const void* k_pool;
   const void* v_pool;
@@ -88,9 +101,9 @@ struct DecodeArgs {
   int32_t group_piece_keys;
   int32_t bf16;
   float scale_log2;  // softmax scale * log2(e)
-  // [max_splits * num_seqs] work order of the partial kernel, written by a
-  // plan kernel launched before it; null: every (piece, request, head) of
-  // the grid in piece-major order
+  // [max_splits * num_seqs] work order of the partial kernel, written before
+  // it runs (plan.h); null: every (piece, request, head) of the grid in
+  // piece-major order
   int4* plan;
 };
 
@@ -120,6 +133,9 @@ struct ExtendArgs {
   int32_t ws_pieces;           // prefix: workspace row stride in pieces
   int32_t skip_single;         // extend: leave requests with one new row to the decode kernels
   float scale_log2;
+  // prefix: when plan.plan is set, one more work-group writes the work order
+  // of the decode partial kernel that follows
+  PlanArgs plan;
 };
 
 // Short chunks (parallel verification of drafted tokens): split-K over keys,
@@ -166,6 +182,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_rope_store(const RopeArgs& a, hipStream_t stream);
 // Return hipErrorInvalidValue for an instantiation that does not exist
 // (the ABI layer validates first, so this is a guard, not a code path).
+hipError_t launch_decode_plan(const PlanArgs& p, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);

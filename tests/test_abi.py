@@ -97,7 +97,7 @@ def test_decode_validation():
         assert decode(p, fn, Lmax=-1) == SHAPE
         assert decode(p, fn, stride=10) == SHAPE  # 10 * 16 < 1000
         assert decode(p, fn, split=100) == SHAPE
-        assert decode(p, fn, split=2048) == SHAPE
+        assert decode(p, fn, split=2112) == SHAPE  # above the 2048-key maximum
         assert decode(p, fn, q=0) == NULL
         assert decode(p, fn, pt=0) == NULL
         assert decode(p, fn, sl=0) == NULL
@@ -113,9 +113,9 @@ def test_decode_validation():
 
 def test_decode_workspace_size_matches_layout():
     lib = pa.load()
-    # 256 requests, 32/8 heads, D=128, 8192 keys: automatic split 1024 -> 8 pieces
-    assert lib.pa_decode_split_tokens(256, 8, 8192) == 1024
-    S = 8
+    # 256 requests, 32/8 heads, D=128, 8192 keys: automatic split 2048 -> 4 pieces
+    assert lib.pa_decode_split_tokens(256, 8, 8192) == 2048
+    S = 4
     rows = 256 * 32 * S
     a256 = lambda x: (x + 255) // 256 * 256
     # partials, log-sum-exps, then the work order (int32 x 4 per piece and request)
@@ -131,14 +131,14 @@ def test_decode_workspace_size_matches_layout():
     (4, 1, 64, 64),        # tiny decode: one piece
     (32, 2, 640, 256),     # Qwen2.5-0.5B shape: too small to fill the chip, 256-key pieces
     (64, 8, 2048, 256),    # Qwen3-0.6B shape: 512 units x 8 pieces reach 4096 work-groups
-    (256, 8, 8192, 1024),  # Qwen3-8B shape
+    (256, 8, 8192, 2048),  # Qwen3-8B shape
     (1, 8, 65536, 128),    # one long request: 8 heads x 512 pieces
     (1, 1, 100000, 256),
     (0, 8, 100, 64),
 ])
 def test_automatic_split(B, H, L, expect):
     s = pa.load().pa_decode_split_tokens(B, H, L)
-    assert s == expect and s % 64 == 0 and 64 <= s <= 1024
+    assert s == expect and s % 64 == 0 and 64 <= s <= 2048
 
 
 def test_extend_validation():
@@ -200,7 +200,7 @@ def test_cascade_plan_and_workspace():
     # large groups of group-1 heads (128 rows per work-group): 2 row blocks
     assert lib.pa_cascade_piece_keys(1, 200, 8, 8, 65536) == 65536 // 16
     B, Hq, D, L, msh = 256, 32, 128, 8192, 1024
-    S, NP = 8, 2
+    S, NP = 4, 2  # automatic split 2048; prefix pieces of 512 keys
     rows = B * Hq * (S + NP)
     a256 = lambda x: (x + 255) // 256 * 256
     expect = a256(rows * D * 4) + a256(rows * 4) + a256(S * B * 16)
@@ -282,6 +282,7 @@ def test_verify_validation():
     assert verify(p, qmax=-1) == SHAPE
     assert verify(p, stride=10) == SHAPE
     assert verify(p, split=100) == SHAPE
+    assert verify(p, split=2048) == SHAPE  # verify pieces hold at most 1024 keys
     assert verify(p, q=0) == NULL
     assert verify(p, qi=0) == NULL
     assert verify(p, out=FAKE + 4) == SHAPE

@@ -152,6 +152,7 @@ DECODE_SWEEP = [
     ([1, 33, 257], 4, 1, 128, 64, "f32", 0),            # fp32, group 4 x 128
     ([0, 5, 0, 40], 8, 2, 128, 16, "bf16", 0),          # empty requests
     ([4097], 32, 8, 128, 16, "bf16", 0),                # one long request
+    ([1, 2047, 2048, 2049, 4097], 32, 8, 128, 16, "bf16", 2048),  # largest pieces
 ]
 
 

@@ -16,7 +16,7 @@ from gpu_helpers import assert_close, bits, f64, fresh, gpu_cascade, gpu_decode,
 
 pytestmark = pytest.mark.gpu
 
-SPLIT = 64  # keys per piece; with these lengths every batch below has >= 8192 work-groups
+SPLIT = 64  # keys per piece; every batch below has at least 8192 work-groups (work order from 6144 on)
 
 
 def banner(msg):
@@ -54,7 +54,7 @@ def test_large_decode_batch_matches_oracle(B, hi):
     # the same requests in a small batch run in grid order: identical bits
     seqs = sorted(set(range(0, B, 13)) | set(zero[:5]))
     sub = wl.subset(seqs)
-    assert len(seqs) * 8 * ((sub.max_seq_len + SPLIT - 1) // SPLIT) < 8192
+    assert len(seqs) * 8 * ((sub.max_seq_len + SPLIT - 1) // SPLIT) < 6144
     out_sub = gpu_decode(sub, fresh(sub), split=SPLIT)
     assert bits(out_sub) == bits(out[seqs])
 
@@ -95,3 +95,37 @@ def test_large_cascade_batch_matches_oracle():
     print(f"[result] max abs err {err:.3g}", flush=True)
     again = gpu_cascade(wl, dw, split=SPLIT, piece_keys=64)
     assert bits(again) == bits(out)
+
+
+def test_largest_pieces_in_work_order():
+    """2048-key pieces (the largest split) on a batch large enough for the
+    work order, lengths around the piece boundaries."""
+    B = 260
+    rng = np.random.default_rng(90)
+    lens = rng.integers(1, 601, B)  # mostly short: the few long requests set the grid
+    lens[:8] = [1, 2047, 2048, 2049, 4095, 4096, 4097, 6000]
+    lens = [int(x) for x in lens]
+    banner(f"decode B={B} lengths<= 6000 split 2048")
+    wl = W.make_custom(lens, 32, 8, 128, 16, dtype="bf16", seed=91)
+    assert B * 8 * ((wl.max_seq_len + 2047) // 2048) >= 6144
+    dw = fresh(wl)
+    out = gpu_decode(wl, dw, split=2048)
+    kp, vp = stored_oracle_pools(wl)
+    ref = oracle.decode(wl.q, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    err = assert_close(f64(out), ref, "decode split 2048")
+    print(f"[result] max abs err {err:.3g}", flush=True)
+
+
+def test_large_cascade_without_groups():
+    """No shared pages: the cascade's first stage only writes the work order
+    of the own-keys pass (no prefix kernel runs)."""
+    B = 900
+    lens = lengths(B, 300, seed=85)
+    banner(f"cascade B={B} without groups, split {SPLIT}")
+    wl = W.make_custom(lens, 16, 8, 64, 16, dtype="bf16", seed=86)
+    dw = fresh(wl)
+    out = gpu_cascade(wl, dw, split=SPLIT)
+    kp, vp = stored_oracle_pools(wl)
+    ref = oracle.decode(wl.q, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    err = assert_close(f64(out), ref, "cascade without groups")
+    print(f"[result] max abs err {err:.3g}", flush=True)

@@ -452,7 +452,8 @@ def main():
         dom_bytes = len(own) * slot_bytes + q_bytes + 4 * pages_read + 8 * B
     else:
         pages_read = int(sum((int(L) + P - 1) // P for L in wl.seq_lens))
-        dom_kernel, dom_ms = "decode_partial_kernel<bf16, D=128, G=4>", stage_ms["partial"]
+        # the partial stage is the work-order kernel (one work-group) and the partial kernel
+        dom_kernel, dom_ms = "decode_plan_kernel + decode_partial_kernel<bf16, D=128, G=4>", stage_ms["partial"]
         dom_bytes = kv_unique + q_bytes + 4 * pages_read + 4 * B
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = read_traffic(args.path)

@@ -206,8 +206,10 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The two kernels of pa_decode, callable one at a time (same arguments).
- * pa_decode_partial writes, for every request with more than one piece, the
+ * The two stages of pa_decode, callable one at a time (same arguments).
+ * pa_decode_partial (on large batches a one-work-group kernel that writes
+ * the order of the pieces into the workspace, then the partial kernel)
+ * writes, for every request with more than one piece, the
  * normalised output and log2-sum-exp of each piece into the workspace, and
  * writes `out` directly for requests with exactly one piece.
  * pa_decode_combine merges the pieces into `out` for requests with more than
@@ -256,6 +258,9 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
  *   1. per (group, KV head, key piece of prefix_piece_keys keys): every
  *      member's query heads of the KV head against the group's prefix keys,
  *      on the matrix cores (each tile of shared K/V is read once per group);
+ *      on large batches one more work-group of this kernel (or, with no
+ *      prefix pass, a kernel of its own) writes the order in which kernel 2
+ *      takes its pieces into the workspace;
  *   2. per (request, KV head, piece of split_tokens keys): the request's own
  *      keys shared_lens[b] .. seq_lens[b] - 1, as in pa_decode_partial;
  *   3. per (request, query head): merge of both sets of pieces by
@@ -303,9 +308,11 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
 
 /*
  * The three kernels of pa_decode_cascade, callable one at a time in this
- * order (same arguments; each validates them all).  _prefix enqueues kernel
- * 1 (nothing when there is no prefix pass), _suffix kernel 2, _combine
- * kernel 3.
+ * order on one workspace (same arguments; each validates them all).
+ * _prefix enqueues kernel 1 (with no prefix pass, only the work order of
+ * kernel 2 when it has one, else nothing), _suffix kernel 2, _combine kernel
+ * 3.  Kernel 2 reads the work order _prefix wrote; an order written for
+ * another batch gives wrong rows but no access outside the requests' pages.
  */
 pa_status pa_decode_cascade_prefix(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,

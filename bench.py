@@ -433,6 +433,27 @@ def main():
     log(f"decode ({args.path}): {ms_step * 1e3:.1f} us/step; " +
         ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in stage_ms.items()) + f" (wall {wall:.3f}s)")
 
+    # The same step captured once into a HIP graph and replayed (how a serving
+    # loop would launch it): the launch gaps between its kernels shrink.  The
+    # replayed output must equal the eager one bit for bit.
+    eager_out = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_same = bool(torch.equal(out.view(torch.int16), eager_out.view(torch.int16)))
+    ms_graph = _time(torch, stream, graph.replay, args.steps)
+    del graph
+
     kv_unique = wl.kv_bytes_unique()
     kv_logical = wl.kv_bytes_logical()
     slot_bytes = 2 * Hkv * D * wl.elem_bytes
@@ -485,6 +506,10 @@ def main():
         "kv_bytes_unique": kv_unique,
         "kv_bytes_logical": kv_logical,
         "kernel_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "graph_replay": {"ms_per_step": round(ms_graph, 5),
+                         "GBps_unique": round(kv_unique / (ms_graph * 1e-3) / 1e9, 2),
+                         "pct_of_hbm_peak": round(100 * kv_unique / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                         "same_bits_as_eager": graph_same},
         "roofline": {
             "kernel": dom_kernel,
             "bound": "hbm",

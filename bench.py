@@ -38,11 +38,16 @@ PROFILE_COUNTERS = {
     "cascade": os.path.join(ROOT, "profiles", "decode_partial_own_keys_qwen3_8b_radix_counters.txt"),
     "plain": os.path.join(ROOT, "profiles", "decode_partial_qwen3_8b_radix_counters.txt"),
     "extend": os.path.join(ROOT, "profiles", "extend_qwen3_8b_extend_counters.txt"),
+    "rope": os.path.join(ROOT, "profiles", "rope_store_qwen3_8b_extend_rows_counters.txt"),
+    "verify": os.path.join(ROOT, "profiles", "verify_qwen3_8b_verify_counters.txt"),
 }
 _CSRC = os.path.join(ROOT, "paged_kv_attention_11_amd", "csrc")
 DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("decode.hip", "device.h", "internal.h")]
 EXTEND_SOURCES = [os.path.join(_CSRC, f) for f in ("extend.hip", "mfma_tile.h", "device.h", "internal.h")]
-KERNEL_SOURCES = {"cascade": DECODE_SOURCES, "plain": DECODE_SOURCES, "extend": EXTEND_SOURCES}
+ROPE_SOURCES = [os.path.join(_CSRC, f) for f in ("rope.hip", "device.h", "internal.h")]
+VERIFY_SOURCES = [os.path.join(_CSRC, f) for f in ("verify.hip", "mfma_tile.h", "device.h", "internal.h")]
+KERNEL_SOURCES = {"cascade": DECODE_SOURCES, "plain": DECODE_SOURCES, "extend": EXTEND_SOURCES,
+                  "rope": ROPE_SOURCES, "verify": VERIFY_SOURCES}
 
 
 def parse():
@@ -204,7 +209,7 @@ def bench_rope(pa, W, torch, np, stream, iters):
     gbps = alg / (ms * 1e-3) / 1e9
     return {"workload": "qwen3_8b_extend (4096 new rows)", "kernel_us": round(ms * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": read_traffic("rope"),
                          "algorithmic_bytes_per_launch": int(alg)}}
 
 
@@ -253,7 +258,7 @@ def bench_verify(pa, W, torch, np, stream, iters):
             "kernel_us": round(ms * 1e3, 2), "extend_us": round(ems * 1e3, 2),
             "rows_per_s": round(int(vw.q_indptr[-1]) / (ms * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": read_traffic("verify"),
                          "algorithmic_bytes_per_launch": int(alg),
                          "note": "verify kernel + its combine; K/V counted once per request"}}
 

@@ -162,15 +162,27 @@ pa_status pa_rope_kv_store(const pa_kv_pool* pool, const void* q, int32_t num_q_
 
 /*
  * Decode split plan.  The key range of each request is cut into consecutive
- * pieces of split_tokens keys; each (request, KV head, piece) is one unit of
- * work, and a second kernel merges the pieces by log-sum-exp weights.
- * pa_decode_split_tokens returns the piece length the library chooses from
- * the host-side sizes alone (a multiple of 64, at most 2048).  Every decode
- * call takes a split_tokens argument: 0 means "this automatic choice", any
- * other value must be a multiple of 64 in [64, 2048].  The result depends on
- * the split only through floating-point rounding.
+ * pieces of split_tokens keys; each (request, piece, block of KV heads) is one
+ * unit of work, and a second kernel merges the pieces by log-sum-exp weights
+ * (the online softmax of the Triton backend in the Mini-SGLang README,
+ * yangyonggit fork, Reference Attention Backends, cut into independent
+ * pieces).  pa_decode_split_tokens returns the piece length the library
+ * chooses from the host-side sizes alone (a multiple of 64, at most 2048).
+ * Every decode call takes a split_tokens argument: 0 means "this automatic
+ * choice", any other value must be a multiple of 64 in [64, 2048].  The
+ * result depends on the split only through floating-point rounding.
+ *
+ * pa_decode_heads_per_block returns how many neighbouring KV heads one unit
+ * serves for these sizes (1, 2 or 4, a divisor of num_kv_heads; 0 for invalid
+ * sizes): large batches take several heads per unit, whose loads then cover
+ * neighbouring slices of the same K/V rows, and shorter automatic pieces
+ * (at most 2048 / heads keys).  The choice depends only on these three sizes,
+ * never on split_tokens, and changes no result beyond floating-point
+ * rounding; every decode call (plain, cascade own keys, mixed) uses it.
  */
 int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len);
+int32_t pa_decode_heads_per_block(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                  int32_t split_tokens);
 
 /*
  * Bytes of device workspace pa_decode needs for these sizes and split_tokens
@@ -344,8 +356,8 @@ pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32
  * requests whose chunks are short, as in the verification of drafted tokens:
  * max_q_len * (num_q_heads / num_kv_heads) <= 32.  The keys of each request
  * are split into pieces of split_tokens keys (0 = the automatic choice, as
- * pa_decode_split_tokens' but at most 1024; else a multiple of 64 in
- * [64, 1024]) handled by separate
+ * pa_decode_split_tokens' at one KV head per unit but at most 1024; else a
+ * multiple of 64 in [64, 1024]) handled by separate
  * work-groups, each reading a K/V tile once for all rows of the chunk and all
  * query heads of a KV head; a second kernel merges the pieces.
  *   workspace: pa_verify_workspace_bytes(...) bytes, 256-byte aligned

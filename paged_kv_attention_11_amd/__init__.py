@@ -21,7 +21,7 @@ from typing import Optional
 
 __all__ = [
     "PagedAttnError", "library_path", "load", "version", "kv_store", "decode", "decode_partial",
-    "decode_combine", "decode_split_tokens", "decode_workspace_bytes", "extend", "gather",
+    "decode_combine", "decode_split_tokens", "decode_heads_per_block", "decode_workspace_bytes", "extend", "gather",
 ]
 
 _PKG = Path(__file__).resolve().parent
@@ -67,6 +67,7 @@ SIGNATURES = {
     "pa_kv_store": (_i32, [_POOLP, _vp, _vp, _vp, _i64, _vp]),
     "pa_rope_kv_store": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _vp, _vp]),
     "pa_decode_split_tokens": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_heads_per_block": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_partial": (_i32, _DECODE_ARGS),
@@ -214,6 +215,10 @@ def rope_kv_store(k_pool, v_pool, q, k_new, v_new, positions, slot_mapping, cos_
 
 def decode_split_tokens(num_seqs: int, num_kv_heads: int, max_seq_len: int) -> int:
     return load().pa_decode_split_tokens(num_seqs, num_kv_heads, max_seq_len)
+
+
+def decode_heads_per_block(num_seqs: int, num_kv_heads: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    return load().pa_decode_heads_per_block(num_seqs, num_kv_heads, max_seq_len, split_tokens)
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, split_tokens=0) -> int:

@@ -54,23 +54,56 @@ pa_status check_pool(const pa_kv_pool* pool) {
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t max_split) {
+// hb: KV heads per work-group (decode; 1 for verify).  A work-group then
+// covers hb heads of a piece, so the longest piece is kMaxSplitTokens / hb
+// keys: the same key-head rows per work-group as one head of the longest
+// piece.
+int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t max_split, int hb = 1) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return kSplitQuantum;
-  const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  for (int64_t split = max_split; split >= kSplitQuantum; split -= kSplitQuantum)
+  const int64_t units = (int64_t)num_seqs * (num_kv_heads / hb);
+  for (int64_t split = max_split / hb; split >= kSplitQuantum; split -= kSplitQuantum)
     if (units * ((max_seq_len + split - 1) / split) >= kTargetUnits) return (int32_t)split;
   // too small to fill the chip: 256-key pieces, or one piece if shorter
   const int64_t one = (max_seq_len + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
   return (int32_t)(one < kSmallBatchSplit ? one : kSmallBatchSplit);
 }
 
+// KV heads per decode work-group.  The four waves of a work-group serve hb
+// neighbouring KV heads (4 / hb waves each) of the same keys; read-only probes
+// on one MI355X streamed the Qwen3-8B-shaped batch 5% faster with four heads
+// per work-group than with one (6.06 against 5.78 TB/s, 256-byte head slices
+// of 2 KB rows).  A work-group of hb heads covers hb times the bytes per key,
+// so its pieces are hb times shorter for the same number of work-groups; the
+// largest hb dividing num_kv_heads is taken when the batch still fills the
+// chip with full-length pieces at it (kMaxSplitTokens / hb keys), else
+// hb = 1, where small batches keep the most work-groups.  That is the
+// automatic split's choice, which depends on the batch like the split itself.
+// With an explicit split the choice depends only on the split and
+// num_kv_heads (the largest hb with split * hb <= kMaxSplitTokens), so a
+// request's result has the same bits in any batch.
+int decode_heads_per_block(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  for (int hb = 4; hb > 1; hb >>= 1) {
+    if (num_kv_heads % hb != 0) continue;
+    const int64_t split =
+        split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_seq_len, kMaxSplitTokens, hb);
+    if (split_tokens ? split * hb <= kMaxSplitTokens : split * hb >= kMaxSplitTokens) return hb;
+  }
+  return 1;
+}
+
 // The split of a call: split_tokens if valid (a multiple of 64 in
 // [64, max_split]), the automatic choice for 0, -1 otherwise.
 int32_t resolve_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
-                      int32_t max_split = kMaxSplitTokens) {
-  if (split_tokens == 0) return auto_split(num_seqs, num_kv_heads, max_seq_len, max_split);
+                      int32_t max_split = kMaxSplitTokens, int hb = 1) {
+  if (split_tokens == 0) return auto_split(num_seqs, num_kv_heads, max_seq_len, max_split, hb);
   const bool ok = split_tokens >= kSplitQuantum && split_tokens <= max_split && split_tokens % kSplitQuantum == 0;
   return ok ? split_tokens : -1;
+}
+
+// The decode split: resolve_split at the batch's heads per work-group.
+int32_t resolve_decode_split(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  return resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len, kMaxSplitTokens,
+                       decode_heads_per_block(0, num_seqs, num_kv_heads, max_seq_len));
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -84,8 +117,8 @@ constexpr int64_t kPlanMinBlocks = 6144;
 
 size_t plan_bytes(int32_t num_seqs, int64_t S) { return S > 1 ? align256((size_t)num_seqs * S * 16) : 0; }
 
-bool use_plan(int32_t num_seqs, int32_t num_kv_heads, int64_t S) {
-  return S > 1 && (int64_t)num_seqs * num_kv_heads * S >= kPlanMinBlocks;
+bool use_plan(int32_t num_seqs, int32_t num_kv_heads, int64_t S, int hb) {
+  return S > 1 && (int64_t)num_seqs * (num_kv_heads / hb) * S >= kPlanMinBlocks;
 }
 
 size_t workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
@@ -108,8 +141,9 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   if (G > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (pool->dtype == PA_F32 && G * pool->head_dim > 512) return PA_ERR_UNSUPPORTED;
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
-  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
+  const int32_t split = resolve_decode_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
   if (split < 0) return PA_ERR_SHAPE;
+  const int hb = decode_heads_per_block(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
   const int64_t S = (max_seq_len + split - 1) / split;
   if ((int64_t)num_seqs * pool->num_kv_heads * S > (int64_t)INT_MAX) return PA_ERR_SHAPE;
   if (num_seqs > 0) {
@@ -141,11 +175,12 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   a.piece_offset = 0;
   a.ws_pieces = (int32_t)S;
   a.always_partial = 0;
+  a.heads_per_block = hb;
   a.group_lens = nullptr;
   a.group_piece_keys = 1;
   a.bf16 = pool->dtype == PA_BF16;
   a.scale_log2 = scale * kLog2e;
-  a.plan = workspace && use_plan(num_seqs, pool->num_kv_heads, S)
+  a.plan = workspace && use_plan(num_seqs, pool->num_kv_heads, S, hb)
                ? (int4*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float)) +
                          align256(rows * sizeof(float)))
                : nullptr;
@@ -286,14 +321,21 @@ pa_status pa_rope_kv_store(const pa_kv_pool* pool, const void* q, int32_t num_q_
 }
 
 int32_t pa_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
-  return auto_split(num_seqs, num_kv_heads, max_seq_len, kMaxSplitTokens);
+  return resolve_decode_split(0, num_seqs, num_kv_heads, max_seq_len);
+}
+
+int32_t pa_decode_heads_per_block(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                  int32_t split_tokens) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (resolve_decode_split(split_tokens, num_seqs, num_kv_heads, max_seq_len) < 0) return 0;
+  return decode_heads_per_block(split_tokens, num_seqs, num_kv_heads, max_seq_len);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len, int32_t split_tokens) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
     return 0;
-  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
+  const int32_t split = resolve_decode_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
   if (split < 0) return 0;
   return workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, split);
 }
@@ -387,7 +429,7 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
       num_groups < 0 || max_group_size < 0 || max_shared_len < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
+  const int32_t split = resolve_decode_split(split_tokens, num_seqs, num_kv_heads, max_seq_len);
   const int32_t pk = resolve_piece_keys(prefix_piece_keys, num_groups, max_group_size,
                                         num_q_heads / num_kv_heads, num_kv_heads, max_shared_len);
   if (split < 0 || pk < 0) return 0;
@@ -420,7 +462,8 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
   if ((int64_t)prefix_pt_stride * pool->page_size < max_shared_len) return PA_ERR_SHAPE;
   if (max_group_size > num_seqs) return PA_ERR_SHAPE;
-  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
+  const int32_t split = resolve_decode_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
+  const int hb = decode_heads_per_block(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len);
   const int32_t pk = resolve_piece_keys(prefix_piece_keys, num_groups, max_group_size, G, pool->num_kv_heads,
                                         max_shared_len);
   if (split < 0 || pk < 0) return PA_ERR_SHAPE;
@@ -465,11 +508,12 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   a.piece_offset = (int32_t)NP;
   a.ws_pieces = (int32_t)(S + NP);
   a.always_partial = 1;
+  a.heads_per_block = hb;
   a.group_lens = prefix_pass ? shared_lens : nullptr;
   a.group_piece_keys = pk;
   a.bf16 = 1;
   a.scale_log2 = scale * kLog2e;
-  a.plan = use_plan(num_seqs, pool->num_kv_heads, S)
+  a.plan = use_plan(num_seqs, pool->num_kv_heads, S, hb)
                ? (int4*)((char*)lse + align256(rows * sizeof(float)))
                : nullptr;
   // pass 1: each group's shared pages, all members' queries in one tile, and

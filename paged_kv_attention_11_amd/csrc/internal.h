@@ -96,6 +96,7 @@ struct DecodeArgs {
   int32_t piece_offset;  // workspace index of a request's piece 0
   int32_t ws_pieces;     // pieces per (request, head) row of the workspace
   int32_t always_partial;  // 1: never finish a single-piece request in the partial kernel
+  int32_t heads_per_block;  // KV heads one work-group serves (1, 2 or 4; divides num_kv_heads)
   // leading pieces written by the shared-prefix kernel (combine only)
   const int32_t* group_lens;  // [B] keys covered by those pieces, or null
   int32_t group_piece_keys;

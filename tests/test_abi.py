@@ -113,32 +113,63 @@ def test_decode_validation():
 
 def test_decode_workspace_size_matches_layout():
     lib = pa.load()
-    # 256 requests, 32/8 heads, D=128, 8192 keys: automatic split 2048 -> 4 pieces
-    assert lib.pa_decode_split_tokens(256, 8, 8192) == 2048
-    S = 4
+    # 256 requests, 32/8 heads, D=128, 8192 keys: four KV heads per work-group,
+    # automatic split 2048 / 4 = 512 -> 16 pieces
+    assert lib.pa_decode_heads_per_block(256, 8, 8192, 0) == 4
+    assert lib.pa_decode_split_tokens(256, 8, 8192) == 512
+    S = 16
     rows = 256 * 32 * S
     a256 = lambda x: (x + 255) // 256 * 256
     # partials, log-sum-exps, then the work order (int32 x 4 per piece and request)
     expect = a256(rows * 128 * 4) + a256(rows * 4) + a256(S * 256 * 16)
     assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 0) == expect
+    # an explicit split keeps its own piece count
+    S2 = 4
+    rows2 = 256 * 32 * S2
+    assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 2048) == (
+        a256(rows2 * 128 * 4) + a256(rows2 * 4) + a256(S2 * 256 * 16))
     # one piece per request: no work order
     assert lib.pa_decode_workspace_bytes(4, 2, 1, 64, 64, 0) == a256(4 * 2 * 64 * 4) + a256(4 * 2 * 4)
     assert lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192, 100) == 0  # invalid split
     assert lib.pa_decode_workspace_bytes(-1, 32, 8, 128, 8192, 0) == 0
 
 
-@pytest.mark.parametrize("B,H,L,expect", [
-    (4, 1, 64, 64),        # tiny decode: one piece
-    (32, 2, 640, 256),     # Qwen2.5-0.5B shape: too small to fill the chip, 256-key pieces
-    (64, 8, 2048, 256),    # Qwen3-0.6B shape: 512 units x 8 pieces reach 4096 work-groups
-    (256, 8, 8192, 2048),  # Qwen3-8B shape
-    (1, 8, 65536, 128),    # one long request: 8 heads x 512 pieces
-    (1, 1, 100000, 256),
-    (0, 8, 100, 64),
+@pytest.mark.parametrize("B,H,L,expect,hb", [
+    (4, 1, 64, 64, 1),          # tiny decode: one piece
+    (32, 2, 640, 256, 1),       # Qwen2.5-0.5B shape: too small to fill the chip, 256-key pieces
+    (64, 8, 2048, 256, 1),      # Qwen3-0.6B shape: 512 units x 8 pieces reach 4096 work-groups
+    (256, 8, 8192, 512, 4),     # Qwen3-8B shape: 4 heads per work-group, 512 units x 16 pieces
+    (512, 2, 8192, 1024, 2),    # 2 KV heads: pairs, 512 units x 8 pieces
+    (256, 6, 8192, 1024, 2),    # 6 KV heads: pairs (4 does not divide 6)
+    (2048, 1, 8192, 2048, 1),   # one KV head
+    (1, 8, 65536, 128, 1),      # one long request: 8 heads x 512 pieces
+    (1, 1, 100000, 256, 1),
+    (0, 8, 100, 64, 1),
 ])
-def test_automatic_split(B, H, L, expect):
-    s = pa.load().pa_decode_split_tokens(B, H, L)
+def test_automatic_split(B, H, L, expect, hb):
+    lib = pa.load()
+    s = lib.pa_decode_split_tokens(B, H, L)
     assert s == expect and s % 64 == 0 and 64 <= s <= 2048
+    assert lib.pa_decode_heads_per_block(B, H, L, 0) == hb
+    assert H % hb == 0
+
+
+@pytest.mark.parametrize("H,split,hb", [
+    (8, 64, 4), (8, 512, 4), (8, 576, 2), (8, 1024, 2), (8, 1088, 1), (8, 2048, 1),
+    (2, 64, 2), (6, 512, 2), (1, 64, 1), (3, 64, 1),
+])
+def test_heads_per_block_with_explicit_split(H, split, hb):
+    # depends on the split and the head count only: the same for any batch
+    lib = pa.load()
+    for B, L in ((1, 64), (4, 1000), (3000, 8192)):
+        assert lib.pa_decode_heads_per_block(B, H, L, split) == hb
+
+
+def test_heads_per_block_invalid_arguments():
+    lib = pa.load()
+    assert lib.pa_decode_heads_per_block(-1, 8, 100, 0) == 0
+    assert lib.pa_decode_heads_per_block(4, 0, 100, 0) == 0
+    assert lib.pa_decode_heads_per_block(4, 8, 100, 100) == 0  # not a multiple of 64
 
 
 def test_extend_validation():
@@ -200,7 +231,7 @@ def test_cascade_plan_and_workspace():
     # large groups of group-1 heads (128 rows per work-group): 2 row blocks
     assert lib.pa_cascade_piece_keys(1, 200, 8, 8, 65536) == 65536 // 16
     B, Hq, D, L, msh = 256, 32, 128, 8192, 1024
-    S, NP = 4, 2  # automatic split 2048; prefix pieces of 512 keys
+    S, NP = 16, 2  # automatic split 512 (four KV heads per work-group); prefix pieces of 512 keys
     rows = B * Hq * (S + NP)
     a256 = lambda x: (x + 255) // 256 * 256
     expect = a256(rows * D * 4) + a256(rows * 4) + a256(S * B * 16)

@@ -69,25 +69,32 @@ int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, 
 }
 
 // KV heads per decode work-group.  The four waves of a work-group serve hb
-// neighbouring KV heads (4 / hb waves each) of the same keys; read-only probes
-// on one MI355X streamed the Qwen3-8B-shaped batch 5% faster with four heads
-// per work-group than with one (6.06 against 5.78 TB/s, 256-byte head slices
-// of 2 KB rows).  A work-group of hb heads covers hb times the bytes per key,
-// so its pieces are hb times shorter for the same number of work-groups; the
-// largest hb dividing num_kv_heads is taken when the batch still fills the
-// chip with full-length pieces at it (kMaxSplitTokens / hb keys), else
-// hb = 1, where small batches keep the most work-groups.  That is the
-// automatic split's choice, which depends on the batch like the split itself.
-// With an explicit split the choice depends only on the split and
-// num_kv_heads (the largest hb with split * hb <= kMaxSplitTokens), so a
-// request's result has the same bits in any batch.
+// neighbouring KV heads (4 / hb waves each) of the same keys, so their loads
+// cover neighbouring slices of the same K/V rows at about the same time;
+// pieces are then at most kMaxSplitTokens / hb keys.  Measured on one MI355X
+// on the Qwen3-8B-shaped radix batch (8 KV heads, each request's own keys,
+// in the work order), microseconds per launch: one head, 2048-key pieces 402;
+// two heads, 1024/1536/2048 keys 384/381/386; four heads, 512/768/1024/1536
+// keys 394/389/380/407.  The plain decode of the same batch, which reads the
+// shared prefix pages of a group through the L2 of the XCDs that run its
+// head blocks, took 495 us with one head, 471-475 with two and 486-494 with
+// four (its head blocks then spread over four XCDs instead of two).  The
+// automatic split therefore takes pairs of heads when num_kv_heads is even
+// and the batch fills the chip with full pieces (1024 keys), else one head,
+// where small batches keep the most work-groups; that choice depends on the
+// batch like the split itself.  With an explicit split the choice depends
+// only on the split and num_kv_heads (the most heads, up to four, with
+// split * hb <= kMaxSplitTokens), so a request's result has the same bits in
+// any batch.
 int decode_heads_per_block(int32_t split_tokens, int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
-  for (int hb = 4; hb > 1; hb >>= 1) {
-    if (num_kv_heads % hb != 0) continue;
-    const int64_t split =
-        split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_seq_len, kMaxSplitTokens, hb);
-    if (split_tokens ? split * hb <= kMaxSplitTokens : split * hb >= kMaxSplitTokens) return hb;
+  if (split_tokens) {
+    for (int hb = 4; hb > 1; hb >>= 1)
+      if (num_kv_heads % hb == 0 && (int64_t)split_tokens * hb <= kMaxSplitTokens) return hb;
+    return 1;
   }
+  if (num_kv_heads % 2 == 0 && auto_split(num_seqs, num_kv_heads, max_seq_len, kMaxSplitTokens, 2) * 2 >=
+                                   kMaxSplitTokens)
+    return 2;
   return 1;
 }
 
@@ -111,14 +118,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Work order of the decode partial kernel (a plan kernel lists the pieces
 // that exist, longest first).  The plan kernel is one more launch of a few
 // microseconds, so it is used only on grids of at least kPlanMinBlocks
-// work-groups; the workspace always has room for it when there is more than
-// one piece per request.
+// (request, KV head, piece) units, whatever the heads per work-group (a grid
+// of 4096 work-groups of two or four heads each ran 20-25% slower in grid
+// order than in the work order on the Qwen3-8B-shaped radix batch); the
+// workspace always has room for it when there is more than one piece per
+// request.
 constexpr int64_t kPlanMinBlocks = 6144;
 
 size_t plan_bytes(int32_t num_seqs, int64_t S) { return S > 1 ? align256((size_t)num_seqs * S * 16) : 0; }
 
-bool use_plan(int32_t num_seqs, int32_t num_kv_heads, int64_t S, int hb) {
-  return S > 1 && (int64_t)num_seqs * (num_kv_heads / hb) * S >= kPlanMinBlocks;
+bool use_plan(int32_t num_seqs, int32_t num_kv_heads, int64_t S) {
+  return S > 1 && (int64_t)num_seqs * num_kv_heads * S >= kPlanMinBlocks;
 }
 
 size_t workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
@@ -180,7 +190,7 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   a.group_piece_keys = 1;
   a.bf16 = pool->dtype == PA_BF16;
   a.scale_log2 = scale * kLog2e;
-  a.plan = workspace && use_plan(num_seqs, pool->num_kv_heads, S, hb)
+  a.plan = workspace && use_plan(num_seqs, pool->num_kv_heads, S)
                ? (int4*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float)) +
                          align256(rows * sizeof(float)))
                : nullptr;
@@ -513,7 +523,7 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   a.group_piece_keys = pk;
   a.bf16 = 1;
   a.scale_log2 = scale * kLog2e;
-  a.plan = use_plan(num_seqs, pool->num_kv_heads, S, hb)
+  a.plan = use_plan(num_seqs, pool->num_kv_heads, S)
                ? (int4*)((char*)lse + align256(rows * sizeof(float)))
                : nullptr;
   // pass 1: each group's shared pages, all members' queries in one tile, and

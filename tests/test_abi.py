@@ -113,11 +113,11 @@ def test_decode_validation():
 
 def test_decode_workspace_size_matches_layout():
     lib = pa.load()
-    # 256 requests, 32/8 heads, D=128, 8192 keys: four KV heads per work-group,
-    # automatic split 2048 / 4 = 512 -> 16 pieces
-    assert lib.pa_decode_heads_per_block(256, 8, 8192, 0) == 4
-    assert lib.pa_decode_split_tokens(256, 8, 8192) == 512
-    S = 16
+    # 256 requests, 32/8 heads, D=128, 8192 keys: two KV heads per work-group,
+    # automatic split 2048 / 2 = 1024 -> 8 pieces
+    assert lib.pa_decode_heads_per_block(256, 8, 8192, 0) == 2
+    assert lib.pa_decode_split_tokens(256, 8, 8192) == 1024
+    S = 8
     rows = 256 * 32 * S
     a256 = lambda x: (x + 255) // 256 * 256
     # partials, log-sum-exps, then the work order (int32 x 4 per piece and request)
@@ -138,7 +138,10 @@ def test_decode_workspace_size_matches_layout():
     (4, 1, 64, 64, 1),          # tiny decode: one piece
     (32, 2, 640, 256, 1),       # Qwen2.5-0.5B shape: too small to fill the chip, 256-key pieces
     (64, 8, 2048, 256, 1),      # Qwen3-0.6B shape: 512 units x 8 pieces reach 4096 work-groups
-    (256, 8, 8192, 512, 4),     # Qwen3-8B shape: 4 heads per work-group, 512 units x 16 pieces
+    (256, 8, 8192, 1024, 2),    # Qwen3-8B shape: pairs of heads, 1024 units x 8 pieces
+    (96, 8, 8192, 1600, 1),     # pairs would need 768-key pieces to fill the chip: one head, 768 units x 6
+    (256, 4, 8192, 1024, 2),    # 4 KV heads: pairs, 512 units x 8 pieces
+    (128, 4, 8192, 1152, 1),    # half as many requests: one head, 512 units x 8 pieces
     (512, 2, 8192, 1024, 2),    # 2 KV heads: pairs, 512 units x 8 pieces
     (256, 6, 8192, 1024, 2),    # 6 KV heads: pairs (4 does not divide 6)
     (2048, 1, 8192, 2048, 1),   # one KV head
@@ -231,7 +234,7 @@ def test_cascade_plan_and_workspace():
     # large groups of group-1 heads (128 rows per work-group): 2 row blocks
     assert lib.pa_cascade_piece_keys(1, 200, 8, 8, 65536) == 65536 // 16
     B, Hq, D, L, msh = 256, 32, 128, 8192, 1024
-    S, NP = 16, 2  # automatic split 512 (four KV heads per work-group); prefix pieces of 512 keys
+    S, NP = 8, 2  # automatic split 1024 (two KV heads per work-group); prefix pieces of 512 keys
     rows = B * Hq * (S + NP)
     a256 = lambda x: (x + 255) // 256 * 256
     expect = a256(rows * D * 4) + a256(rows * 4) + a256(S * B * 16)

@@ -62,7 +62,7 @@ def test_explicit_split_matches_oracle(Hq, Hkv, D, P, dtype, split, hb):
 
 def big_batch(seed, radix=None):
     """160 requests, mostly short, a few up to 8192 keys: the automatic split
-    takes four KV heads per work-group and 512-key pieces, in the work order."""
+    takes two KV heads per work-group and 1024-key pieces, in the work order."""
     lens = ragged(152, 600, seed=seed, long=[1, 1024, 2047, 4096, 5000, 6001, 7777, 8192])
     return W.make_custom(lens, 32, 8, 128, 16, dtype="bf16", seed=seed, radix=radix)
 
@@ -70,8 +70,8 @@ def big_batch(seed, radix=None):
 def test_automatic_split_of_a_large_batch():
     wl = big_batch(501)
     banner(f"automatic split B={wl.num_seqs} max {wl.max_seq_len}")
-    assert pa().decode_heads_per_block(wl.num_seqs, 8, wl.max_seq_len) == 4
-    assert pa().decode_split_tokens(wl.num_seqs, 8, wl.max_seq_len) == 512
+    assert pa().decode_heads_per_block(wl.num_seqs, 8, wl.max_seq_len) == 2
+    assert pa().decode_split_tokens(wl.num_seqs, 8, wl.max_seq_len) == 1024
     dw = fresh(wl)
     out = gpu_decode(wl, dw)
     err = assert_close(f64(out), oracle_decode(wl), "decode automatic split")
@@ -79,16 +79,22 @@ def test_automatic_split_of_a_large_batch():
     print(f"[result] max abs err {err:.3g}", flush=True)
 
 
-def test_cascade_own_keys_with_four_heads_per_work_group():
+def test_cascade_own_keys_with_two_heads_per_work_group():
     wl = big_batch(502, radix=(16, 40))
     banner(f"cascade B={wl.num_seqs} groups of 16 sharing 40 pages")
-    assert pa().decode_heads_per_block(wl.num_seqs, 8, wl.max_seq_len) == 4
-    out = gpu_cascade(wl, fresh(wl))
-    err = assert_close(f64(out), oracle_decode(wl), "cascade automatic split")
+    assert pa().decode_heads_per_block(wl.num_seqs, 8, wl.max_seq_len) == 2
+    dw = fresh(wl)
+    ref = oracle_decode(wl)
+    out = gpu_cascade(wl, dw)
+    err = assert_close(f64(out), ref, "cascade automatic split")
     print(f"[result] max abs err {err:.3g}", flush=True)
+    # four heads per work-group at an explicit 512-key split
+    assert pa().decode_heads_per_block(wl.num_seqs, 8, wl.max_seq_len, 512) == 4
+    err = assert_close(f64(gpu_cascade(wl, dw, split=512)), ref, "cascade split 512")
+    print(f"[result] split 512: max abs err {err:.3g}", flush=True)
 
 
-def test_mixed_batch_with_four_heads_per_work_group():
+def test_mixed_batch_with_two_heads_per_work_group():
     wl0 = big_batch(503)
     lens = [int(x) for x in wl0.seq_lens]
     n_new = [1 if L > 0 else 0 for L in lens]
@@ -98,7 +104,7 @@ def test_mixed_batch_with_four_heads_per_work_group():
             n_new[b] = int(min(lens[b], rng.integers(2, 100)))
     wl = W.make_custom(lens, 32, 8, 128, 16, dtype="bf16", kind="extend", n_new=n_new, seed=505)
     banner(f"mixed B={wl.num_seqs}: {sum(n > 1 for n in n_new)} chunks")
-    assert pa().decode_heads_per_block(wl.num_seqs, 8, wl.max_seq_len) == 4
+    assert pa().decode_heads_per_block(wl.num_seqs, 8, wl.max_seq_len) == 2
     dw = fresh(wl)
     out = pa().attend_mixed(dw.q, dw.q_indptr, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_q_len,
                             wl.max_seq_len, wl.scale)

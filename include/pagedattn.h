@@ -319,12 +319,20 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three kernels of pa_decode_cascade, callable one at a time in this
- * order on one workspace (same arguments; each validates them all).
- * _prefix enqueues kernel 1 (with no prefix pass, only the work order of
- * kernel 2 when it has one, else nothing), _suffix kernel 2, _combine kernel
- * 3.  Kernel 2 reads the work order _prefix wrote; an order written for
- * another batch gives wrong rows but no access outside the requests' pages.
+ * The stages of pa_decode_cascade, one kernel each, callable one at a time on
+ * one workspace (same arguments; each validates them all):
+ *   _order    the work order of kernel 2 (a one-work-group kernel; nothing
+ *             when kernel 2 runs without one, i.e. on small batches);
+ *   _prefix   kernel 1 alone (nothing when there is no shared prefix);
+ *   _suffix   kernel 2: reads the work order _order wrote;
+ *   _combine  kernel 3: after both _prefix and _suffix.
+ * _order must precede _suffix; _prefix writes other parts of the workspace
+ * than _order and _suffix and reads nothing they write, so it may run
+ * concurrently with them on another stream (after the store of the new rows
+ * on both, and with _combine after all three).  Called as pa_decode_cascade,
+ * the work order is written by one extra work-group of kernel 1 instead (one
+ * launch fewer).  A work order written for another batch gives wrong rows but
+ * no access outside the requests' pages.
  */
 pa_status pa_decode_cascade_prefix(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
@@ -350,6 +358,14 @@ pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32
                                     const int32_t* shared_lens, int32_t max_shared_len, float scale,
                                     int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+pa_status pa_decode_cascade_order(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                                  const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
+                                  int32_t num_groups, int32_t max_group_size,
+                                  const int32_t* prefix_page_table, int32_t prefix_pt_stride,
+                                  const int32_t* shared_lens, int32_t max_shared_len, float scale,
+                                  int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * pa_verify: the result of pa_extend (same arguments and semantics) for

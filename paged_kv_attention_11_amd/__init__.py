@@ -79,6 +79,7 @@ SIGNATURES = {
     "pa_decode_cascade_prefix": (_i32, _CASCADE_ARGS),
     "pa_decode_cascade_suffix": (_i32, _CASCADE_ARGS),
     "pa_decode_cascade_combine": (_i32, _CASCADE_ARGS),
+    "pa_decode_cascade_order": (_i32, _CASCADE_ARGS),
     "pa_attend_mixed": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz,
                                _vp]),
     "pa_verify_workspace_bytes": (_sz, [_i32] * 7),
@@ -320,8 +321,10 @@ def decode_cascade(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, group_s
                    split_tokens=0, prefix_piece_keys=0, stream=None, stage=None):
     """Decode of requests that share prefix pages: group j is requests
     group_starts[j]..group_starts[j+1]-1, whose first shared_lens[b] keys sit
-    on prefix_page_table[j].  Same result as decode(...).  `stage` ("prefix",
-    "suffix" or "combine") enqueues only that kernel."""
+    on prefix_page_table[j].  Same result as decode(...).  `stage` ("order",
+    "prefix", "suffix" or "combine") enqueues only that kernel ("order" before
+    "suffix"; "prefix" may run on another stream beside those two; "combine"
+    after all three)."""
     torch = _torch()
     pool = make_pool(k_pool, v_pool)
     _dev(q, "q", torch.bfloat16)

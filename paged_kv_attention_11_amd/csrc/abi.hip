@@ -450,7 +450,12 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
 
 namespace {
 
-enum : unsigned { kStagePrefix = 1, kStageSuffix = 2, kStageCombine = 4, kStageAll = 7 };
+// Stages: the shared-prefix pass, the own-keys pass, the merge, and the own-keys
+// pass's work order.  Called together (pa_decode_cascade), the work order is
+// written by one extra work-group of the shared-prefix pass; called one at a
+// time, each stage is one kernel, so the shared-prefix pass may run on
+// another stream beside the work order and the own-keys pass.
+enum : unsigned { kStagePrefix = 1, kStageSuffix = 2, kStageCombine = 4, kStageOrder = 8, kStageAll = 15 };
 
 // The cascade decode's validation, plan and the enqueueing of the selected
 // stages (all three for pa_decode_cascade).
@@ -527,7 +532,8 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
                ? (int4*)((char*)lse + align256(rows * sizeof(float)))
                : nullptr;
   // pass 1: each group's shared pages, all members' queries in one tile, and
-  // the work order of pass 2 (when it has one)
+  // (all stages in one call) the work order of pass 2 when it has one
+  const bool order_in_prefix = prefix_pass && (stages & kStagePrefix) && (stages & kStageOrder);
   if (prefix_pass && (stages & kStagePrefix)) {
     pa::ExtendArgs e = {};
     e.k_pool = pool->k_pool;
@@ -551,9 +557,11 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
     e.ws_pieces = (int32_t)(S + NP);
     e.scale_log2 = scale * kLog2e;
     e.plan = plan_args(a);  // its extra work-group writes pass 2's work order
+    if (!order_in_prefix) e.plan.plan = nullptr;
     st = hip_status(pa::launch_prefix(e, hs));
     if (st != PA_OK) return st;
-  } else if (stages & kStagePrefix) {
+  }
+  if ((stages & kStageOrder) && !order_in_prefix) {  // no-op when pass 2 has no work order
     st = hip_status(pa::launch_decode_plan(plan_args(a), hs));
     if (st != PA_OK) return st;
   }
@@ -585,6 +593,7 @@ pa_status pa_decode_cascade(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_
 pa_status pa_decode_cascade_prefix(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStagePrefix); }
 pa_status pa_decode_cascade_suffix(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStageSuffix); }
 pa_status pa_decode_cascade_combine(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStageCombine); }
+pa_status pa_decode_cascade_order(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStageOrder); }
 
 #undef PA_CASCADE_PARAMS
 #undef PA_CASCADE_ARGS

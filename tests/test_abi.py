@@ -197,7 +197,7 @@ def cascade(p, q=FAKE, Hq=32, pt=FAKE, stride=64, sl=FAKE, B=32, Lmax=1000, gs=F
                                   pstride, shl, msh, 0.1, split, pk, out, ws, ws_bytes, None)
 
 
-@pytest.mark.parametrize("fn", ["pa_decode_cascade", "pa_decode_cascade_prefix", "pa_decode_cascade_suffix",
+@pytest.mark.parametrize("fn", ["pa_decode_cascade", "pa_decode_cascade_prefix", "pa_decode_cascade_suffix", "pa_decode_cascade_order",
                                 "pa_decode_cascade_combine"])
 def test_cascade_validation(fn):
     p = pool()

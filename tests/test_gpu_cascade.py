@@ -123,8 +123,42 @@ def test_cascade_stages_called_one_at_a_time_match_the_single_call():
     nb = pa().decode_cascade_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                              wl.max_seq_len, gs.numel() - 1, gmax, msh)
     ws = T.empty(nb, dtype=T.uint8, device="cuda")
-    for stage in ("prefix", "suffix", "combine"):
+    for stage in ("order", "prefix", "suffix", "combine"):
         pa().decode_cascade(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, gs, gmax, ppt,
                             shl, msh, wl.scale, out=out, workspace=ws, stage=stage)
     T.cuda.synchronize()
     assert bits(out) == whole
+
+
+def test_cascade_prefix_stage_on_a_second_stream():
+    """The shared-prefix pass on another stream, concurrently with the work
+    order and the own-keys pass: the same bits as the single call, on several
+    steps in a row with a fresh output each time."""
+    banner("cascade prefix stage on a second stream")
+    from gpu_helpers import cascade_device, pa
+
+    wl, dw = named("qwen3_8b_radix")
+    whole = bits(gpu_cascade(wl, dw))
+    gs, ppt, shl, gmax, msh = cascade_device(wl)
+    T = torch()
+    nb = pa().decode_cascade_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                             wl.max_seq_len, gs.numel() - 1, gmax, msh)
+    ws = T.empty(nb, dtype=T.uint8, device="cuda")
+    main = T.cuda.current_stream()
+    side = T.cuda.Stream()
+
+    def stage(name, out):
+        pa().decode_cascade(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, gs, gmax, ppt,
+                            shl, msh, wl.scale, out=out, workspace=ws, stage=name)
+
+    for _ in range(3):
+        out = T.full_like(dw.q, float("nan"))
+        side.wait_stream(main)
+        with T.cuda.stream(side):
+            stage("prefix", out)
+        stage("order", out)
+        stage("suffix", out)
+        main.wait_stream(side)
+        stage("combine", out)
+        T.cuda.synchronize()
+        assert bits(out) == whole

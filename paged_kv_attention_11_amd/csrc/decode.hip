@@ -142,9 +142,10 @@ __device__ __forceinline__ uint4 load16(const void* ptr) {
     return *(const uint4*)ptr;
 }
 
-constexpr int kPlanThreads = 1024;
-
-// The work order of the partial kernel (plan.h), by one work-group.
+// The work order of the partial kernel (plan.h), by one work-group: 256
+// threads for batches of at most 256 requests (one request per thread, and
+// the loops over the waves of the work-group are short), else 1024.
+template <int kPlanThreads>
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const PlanArgs p) {
   build_decode_plan<kPlanThreads>(p);
 }
@@ -459,6 +460,8 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
 // read at once (one per lane), and the partial outputs in batches of eight
 // independent loads, so the merge costs a few memory latencies, not one per
 // piece.
+constexpr int kFewPieces = 16;  // rows of at most this many pieces take the one-round-trip path
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p) {
   constexpr int EPL = D / 64;  // output elements per lane
@@ -489,7 +492,46 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs p)
   float res[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) res[e] = 0.f;
-  if (n > 0) {
+  if (n > 0 && n <= kFewPieces) {
+    // every load issued at once: the log-sum-exps (lane i: piece i) and the
+    // partial outputs of all pieces do not depend on each other, so the merge
+    // waits for one memory round trip instead of three.  Same order of
+    // operations as the general path below.
+    const float l = lane < n ? lse[lane < ng ? lane : lane + off] : -INFINITY;
+    float v[kFewPieces][EPL];
+#pragma unroll
+    for (int k = 0; k < kFewPieces; ++k) {
+      if (k < n) {  // uniform
+        const float* src = op + (int64_t)(k < ng ? k : k + off) * D;
+        if constexpr (EPL == 2) {
+          const float2 x = *(const float2*)src;
+          v[k][0] = x.x;
+          v[k][1] = x.y;
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[k][e] = src[e];
+        }
+      }
+    }
+    const float M = wave_max(l);
+    if (M != -INFINITY) {
+      const float w = (lane < n && l != -INFINITY) ? fast_exp2(l - M) : 0.f;
+      const float wsum = wave_sum(w);
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < kFewPieces; ++k) {
+        if (k < n) {  // uniform
+          const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = wk > 0.f ? fmaf(wk, v[k][e], o[e]) : o[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) res[e] = o[e] / wsum;
+    }
+  } else if (n > 0) {
     // pieces with no visible key (lse = -inf) get weight zero
     float M = -INFINITY;
     for (int c = 0; c < n; c += 64) {
@@ -603,7 +645,10 @@ hipError_t launch_partial_d(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_plan(const PlanArgs& p, hipStream_t stream) {
   if (!p.plan || p.num_seqs <= 0 || p.max_splits <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  if (p.num_seqs <= 256)
+    hipLaunchKernelGGL(decode_plan_kernel<256>, dim3(1), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_plan_kernel<1024>, dim3(1), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@ heads, head_dim 128, page 16, bf16; groups of 16 requests share a 1024-token
 prefix): kv_store of the 256 new K/V rows, then the cascade decode (shared
 prefix pass on the matrix cores, each request's own keys through the split-K
 decode kernel, combine), the shared-prefix pass on a second stream beside the
-own-keys pass.  The same calls one after the other on one stream give the
+store, the work order and the own-keys pass.  The same calls one after the other on one stream give the
 per-kernel times.  Inputs are resident in HBM before timing starts.
 The plain decode (partial + combine over every request's whole page list) and
 the chunked-prefill extend call (8 requests, prefix 0..4096 + 512-token
@@ -424,18 +424,31 @@ def main():
             ev[len(stages)].record(stream)
 
     side = torch.cuda.Stream()  # default priority, like every stream here
+    if cascade:
+        # the new rows must not land on a page the prefix pass reads
+        shared_pages = set()
+        for j in range(len(starts) - 1):
+            need = int(shl[starts[j]:starts[j + 1]].max(initial=0))
+            shared_pages.update(ppt[j, :(need + P - 1) // P].tolist())
+        new_pages = set((wl.slot_mapping[wl.slot_mapping >= 0] // P).tolist())
+        assert not (shared_pages & new_pages), "a new row lands on a shared prefix page"
 
     def step_overlapped():
         """The timed step.  Cascade: the shared-prefix pass (one latency-bound
-        work-group per compute unit) on a second stream, beside the work order
-        and the HBM-bound own-keys pass; the merge after both."""
+        work-group per compute unit) on a second stream from the start of the
+        step, beside the store, the work order and the HBM-bound own-keys
+        pass; the merge after both.  The prefix pass reads only keys below
+        each request's shared length, on the groups' prefix pages, which this
+        step's store does not write (checked below), so it does not wait for
+        the store, and its work-groups take their compute units before the
+        own-keys pass fills the rest."""
         if not cascade:
             return step()
         cur = torch.cuda.current_stream()
-        pa.kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
         side.wait_stream(cur)
         with torch.cuda.stream(side):
             call("prefix")
+        pa.kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
         call("order")
         call("suffix")
         cur.wait_stream(side)
@@ -534,8 +547,8 @@ def main():
             "description": W.DESCRIPTIONS.get(args.config, args.config),
             "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
             "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "split_tokens": split,
-            "step": "kv_store + " + ("decode_cascade stages (prefix pass on a second stream beside the work "
-                                     "order and the own-keys pass, then combine)" if cascade
+            "step": "kv_store + " + ("decode_cascade stages (prefix pass on a second stream beside the store, "
+                                     "the work order and the own-keys pass, then combine)" if cascade
                                      else "decode_partial + decode_combine"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -328,8 +328,11 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
  *   _combine  kernel 3: after both _prefix and _suffix.
  * _order must precede _suffix; _prefix writes other parts of the workspace
  * than _order and _suffix and reads nothing they write, so it may run
- * concurrently with them on another stream (after the store of the new rows
- * on both, and with _combine after all three).  Called as pa_decode_cascade,
+ * concurrently with them on another stream, with _combine after all three.
+ * _suffix reads the step's new rows, so it follows their store; _prefix reads
+ * only the keys below each request's shared length, so it may even run
+ * beside the store when no new row lands on those prefix pages (a radix
+ * cache writes a new token to a page of its own request).  Called as pa_decode_cascade,
  * the work order is written by one extra work-group of kernel 1 instead (one
  * launch fewer).  A work order written for another batch gives wrong rows but
  * no access outside the requests' pages.

@@ -162,3 +162,48 @@ def test_cascade_prefix_stage_on_a_second_stream():
         stage("combine", out)
         T.cuda.synchronize()
         assert bits(out) == whole
+
+
+def test_cascade_prefix_stage_beside_the_store():
+    """The prefix pass started before the store of the step's new rows, on a
+    second stream (the new rows lie on pages of their own requests, which the
+    prefix pass never reads): the same bits as the single call after the
+    store."""
+    banner("cascade prefix stage beside the store")
+    from gpu_helpers import cascade_device, pa
+
+    wl, dw_stored = named("qwen3_8b_radix")
+    whole = bits(gpu_cascade(wl, dw_stored))
+    starts, ppt_h, shl_h = wl.cascade_inputs()
+    P = wl.page_size
+    shared = set()
+    for j in range(len(starts) - 1):
+        need = int(shl_h[starts[j]:starts[j + 1]].max(initial=0))
+        shared.update(ppt_h[j, :(need + P - 1) // P].tolist())
+    assert not shared & set((wl.slot_mapping[wl.slot_mapping >= 0] // P).tolist())
+    gs, ppt, shl, gmax, msh = cascade_device(wl)
+    T = torch()
+    nb = pa().decode_cascade_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                             wl.max_seq_len, gs.numel() - 1, gmax, msh)
+    ws = T.empty(nb, dtype=T.uint8, device="cuda")
+    main = T.cuda.current_stream()
+    side = T.cuda.Stream()
+    for _ in range(2):
+        dw = W.to_device(wl)  # new rows not stored yet
+        T.cuda.synchronize()
+        out = T.full_like(dw.q, float("nan"))
+
+        def stage(name):
+            pa().decode_cascade(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, gs, gmax,
+                                ppt, shl, msh, wl.scale, out=out, workspace=ws, stage=name)
+
+        side.wait_stream(main)
+        with T.cuda.stream(side):
+            stage("prefix")
+        pa().kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
+        stage("order")
+        stage("suffix")
+        main.wait_stream(side)
+        stage("combine")
+        T.cuda.synchronize()
+        assert bits(out) == whole

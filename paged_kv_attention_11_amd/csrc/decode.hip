@@ -10,12 +10,12 @@
 // softmax per (request, head); this design keeps the online softmax but
 // reorganises the work for an HBM-bound gfx950 kernel:
 //
-//  * Split-K over keys.  Work unit = (request b, KV head g, piece s of
-//    split_tokens keys).  decode_partial_kernel writes the piece's
-//    normalised output o_s and its log2-sum-exp; decode_combine_kernel merges
-//    pieces with weights 2^(lse_s - max lse).  A request with one piece is
-//    finished by the partial kernel directly.
-//  * GQA sharing.  A work-group serves all G query heads of KV head g, so
+//  * Split-K over keys.  Work unit = (request b, block of HB neighbouring KV
+//    heads, piece s of split_tokens keys).  decode_partial_kernel writes the
+//    piece's normalised output o_s and its log2-sum-exp per query head;
+//    decode_combine_kernel merges pieces with weights 2^(lse_s - max lse).  A
+//    request with one piece is finished by the partial kernel directly.
+//  * GQA sharing.  The waves of a KV head serve all G query heads of it, so
 //    every K/V byte is fetched from HBM once per work unit and reused G times
 //    from registers.
 //  * Loads.  Each wave takes 16 keys per iteration.  K is read in a
@@ -159,8 +159,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const PlanArg
 // work-group read neighbouring head slices of the same key rows at about the
 // same time, which streams faster than one head per work-group: read-only
 // probes of the Qwen3-8B-shaped batch (8 KV heads, 256-byte head slices of
-// 2 KB rows) moved 5.78 TB/s with one head x four waves and 6.06 TB/s with
-// four heads x one wave on the same box.
+// 2 KB rows) moved 5.78 TB/s with one head x four waves, 6.09 TB/s with two
+// heads x two waves and 6.02-6.06 TB/s with four heads x one wave.
 template <bool BF16, int D, int G, bool NT, int HB>
 __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_partial_kernel(
     const DecodeArgs p) {

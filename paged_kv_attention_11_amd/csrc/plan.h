@@ -3,9 +3,10 @@
 // the cascade's shared-prefix pass (which runs just before the partial kernel
 // and leaves most of the chip idle).
 //
-// Entry i of the order is the piece that work-groups i * H_kv .. i * H_kv +
-// H_kv - 1 take: {request, piece | kPlanSingle when it is the request's only
-// piece and finishes the output, first key, keys}; keys = 0 marks a request
+// Entry i of the order is the piece that work-groups i * nb .. i * nb + nb - 1
+// take (nb blocks of neighbouring KV heads, one work-group each): {request,
+// piece | kPlanSingle when it is the request's only piece and finishes the
+// output, first key, keys}; keys = 0 marks a request
 // with no keys that gets a zero row; request -1 marks no work.  Order: every
 // full piece (split_tokens keys) in request order, then the shorter last
 // pieces by decreasing key count in classes of kPlanClassKeys keys (request

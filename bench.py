@@ -44,7 +44,7 @@ PROFILE_COUNTERS = {
     "verify": os.path.join(ROOT, "profiles", "verify_qwen3_8b_verify_counters.txt"),
 }
 _CSRC = os.path.join(ROOT, "paged_kv_attention_11_amd", "csrc")
-DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("decode.hip", "device.h", "internal.h")]
+DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("decode.hip", "plan.h", "device.h", "internal.h")]
 EXTEND_SOURCES = [os.path.join(_CSRC, f) for f in ("extend.hip", "mfma_tile.h", "device.h", "internal.h")]
 ROPE_SOURCES = [os.path.join(_CSRC, f) for f in ("rope.hip", "device.h", "internal.h")]
 VERIFY_SOURCES = [os.path.join(_CSRC, f) for f in ("verify.hip", "mfma_tile.h", "device.h", "internal.h")]

@@ -506,6 +506,11 @@ def main():
     torch.cuda.synchronize()
     ms_sequential = start.elapsed_time(end) / args.steps
     stage_ms = {st: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, st in enumerate(stages)}
+    stage_stats = {}
+    for i, st in enumerate(stages):
+        v = np.array([e[i].elapsed_time(e[i + 1]) for e in evs]) * 1e3
+        stage_stats[st] = {"median": round(float(np.median(v)), 2), "min": round(float(v.min()), 2),
+                           "p90": round(float(np.percentile(v, 90)), 2)}
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record(stream)
@@ -593,6 +598,7 @@ def main():
         "kv_bytes_unique": kv_unique,
         "kv_bytes_logical": kv_logical,
         "kernel_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "kernel_us_stats": stage_stats,
         "sequential_ms_per_step": round(ms_sequential, 5),
         "graph_replay": {"ms_per_step": round(ms_graph, 5),
                          "GBps_unique": round(kv_unique / (ms_graph * 1e-3) / 1e9, 2),

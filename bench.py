@@ -352,7 +352,11 @@ def bench_mixed(pa, W, torch, np, stream, iters):
 
 
 def cpu_baseline(wl, target_s):
-    """The oracle, as it stands, on a bounded sample of the workload."""
+    """The oracle, as it stands, in its float32 arithmetic mode (a plain CPU
+    fp32 implementation: gather the pages, then naive softmax attention per
+    request and head), on a bounded sample of the workload.  `cores` is the
+    number of cores it kept busy on average (process CPU time / wall time);
+    the BLAS pool size and the affinity set are reported beside it."""
     import numpy as np
 
     import oracle
@@ -360,30 +364,35 @@ def cpu_baseline(wl, target_s):
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas_threads = 1
     kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping)
     order = np.random.default_rng(0).permutation(wl.num_seqs)
-    done, t_used, nbytes = 0, 0.0, 0
+    done, t_used, cpu_used, nbytes = 0, 0.0, 0.0, 0
     per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
     while done < wl.num_seqs and t_used < target_s:
         k = 4 if done == 0 else max(1, min(wl.num_seqs - done, int(done * (target_s - t_used) / max(t_used, 1e-3))))
         seqs = order[done:done + k]
         sub = wl.subset(seqs)
-        t0 = time.perf_counter()
-        oracle.decode(sub.q, kp, vp, sub.page_table, sub.seq_lens, wl.scale, wl.dtype)
+        t0, c0 = time.perf_counter(), time.process_time()
+        oracle.decode(sub.q, kp, vp, sub.page_table, sub.seq_lens, wl.scale, wl.dtype, acc="f32")
         t_used += time.perf_counter() - t0
+        cpu_used += time.process_time() - c0
         nbytes += int(sub.seq_lens.sum()) * per_tok
         done += k
     return {
         "value": round(nbytes / t_used / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": max(1, int(round(cpu_used / t_used))),
         "kind": "oracle",
-        "sample": f"oracle.decode (float64 numpy) over {done} of {wl.num_seqs} requests of the same workload "
-                  f"({nbytes / 1e9:.3f} GB of K/V read, logical), {t_used:.1f} s; store excluded; "
-                  f"host has {os.cpu_count()} logical CPUs",
+        "sample": f"oracle.decode (numpy, float32 arithmetic) over {done} of {wl.num_seqs} requests of the same "
+                  f"workload ({nbytes / 1e9:.3f} GB of K/V read, logical bytes), {t_used:.1f} s; store excluded",
+        "cores_busy_avg": round(cpu_used / t_used, 2),
+        "blas_threads": int(blas_threads),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "host_cpus": os.cpu_count(),
+        "requests_per_s": round(done / t_used, 2),
     }
 
 
@@ -723,8 +732,13 @@ def main():
     # ---------------- CPU oracle on a bounded sample (rank 0, N=1 only)
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-        log(f"cpu baseline: {result['cpu_baseline']['value']} GB/s in {time.perf_counter() - t0:.1f}s")
+        cb = cpu_baseline(wl, args.cpu_seconds)
+        # the same basis on both sides: logical K/V bytes read per second
+        gpu_logical = wl.kv_bytes_logical() / (result["ms_per_step"] * 1e-3) / 1e9
+        cb["gpu_over_oracle"] = round(gpu_logical / cb["value"], 1)
+        result["cpu_baseline"] = cb
+        log(f"cpu baseline: {cb['value']} GB/s in {time.perf_counter() - t0:.1f}s "
+            f"(GPU / oracle {cb['gpu_over_oracle']}x)")
     else:
         result["cpu_baseline"] = None
 

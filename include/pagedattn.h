@@ -245,7 +245,7 @@ pa_status pa_decode_combine(const pa_kv_pool* pool, const void* q, int32_t num_q
  *   q, out     [q_indptr[num_seqs], num_q_heads, head_dim], bf16, 16-byte
  *              aligned; q_indptr int32 [num_seqs + 1], non-decreasing
  *   max_q_len  host-side upper bound of n_b; max_seq_len of seq_lens.
- * bf16 pools only, head_dim 128 or 64, group size 1, 2, 4 or 8.  Scores and
+ * bf16 pools only, head_dim 128 or 64, group size 1 .. 8.  Scores and
  * the output are accumulated in fp32; softmax weights are rounded to bf16
  * before the weighted sum of V (matrix-core inputs).
  */
@@ -302,7 +302,7 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
  *                       split_tokens) pieces of kernel 2 follow; then, when
  *                       S > 1, the work order of kernel 2 as for pa_decode.
  * bf16 pools only, head_dim 128 or 64, group size (num_q_heads /
- * num_kv_heads) 1, 2, 4 or 8.  A request with seq_len 0 gets a zero row.
+ * num_kv_heads) 1 .. 8.  A request with seq_len 0 gets a zero row.
  */
 int32_t pa_cascade_piece_keys(int32_t num_groups, int32_t max_group_size, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t max_shared_len);
@@ -386,8 +386,8 @@ pa_status pa_decode_cascade_order(const pa_kv_pool* pool, const void* q, int32_t
  *              log2-sum-exp [num_seqs, max_q_len, num_q_heads, S],
  *              S = ceil(max_seq_len / split_tokens).
  * Chunks longer than max_q_len are a contract violation (their extra rows
- * are not computed).  bf16 pools only, head_dim 128 or 64, group size 1, 2,
- * 4 or 8.  Softmax weights are rounded to bf16 before the weighted sum of V.
+ * are not computed).  bf16 pools only, head_dim 128 or 64, group size
+ * 1 .. 8.  Softmax weights are rounded to bf16 before the weighted sum of V.
  */
 size_t pa_verify_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len, int32_t split_tokens);
@@ -411,7 +411,7 @@ pa_status pa_verify(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
  *   max_q_len, max_seq_len: host-side bounds; the grids and the split plan
  *                   depend only on them, so a captured call can be replayed
  *                   with other device-side contents within the same bounds.
- * bf16 pools only, head_dim 128 or 64, group size 1, 2, 4 or 8.
+ * bf16 pools only, head_dim 128 or 64, group size 1 .. 8.
  */
 pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* q_indptr,
                           const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs,
@@ -448,6 +448,34 @@ pa_status pa_check_batch(const pa_kv_pool* pool, const int32_t* page_table, int3
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const int32_t* q_indptr,
                          int32_t max_q_len, const int64_t* slot_mapping, int64_t num_rows, uint32_t* flags,
                          void* stream);
+
+/*
+ * pa_check_cascade: the same kind of debug check for the group description
+ * of pa_decode_cascade (whose kernels take it on trust).  Clears *flags, then
+ * ORs into it:
+ *   PA_CHECK_GROUP_STARTS   group_starts[0] != 0, group_starts[num_groups] !=
+ *                           num_seqs, a decreasing step, or a group larger
+ *                           than max_group_size
+ *   PA_CHECK_SHARED_LEN     a shared_len outside [0, min(seq_len,
+ *                           max_shared_len)] (a shared_len above
+ *                           max_shared_len would make the cascade leave keys
+ *                           out)
+ *   PA_CHECK_PREFIX_PAGE    a page holding a request's shared keys that is
+ *                           not its group's prefix page at that position, or
+ *                           a prefix page id outside [0, num_pages)
+ * It reads only the tables, never a pool page.  With num_groups 0 it only
+ * clears *flags.  The caller reads *flags after synchronising the stream.
+ */
+enum {
+  PA_CHECK_GROUP_STARTS = 32u,
+  PA_CHECK_SHARED_LEN = 64u,
+  PA_CHECK_PREFIX_PAGE = 128u
+};
+pa_status pa_check_cascade(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                           const int32_t* seq_lens, int32_t num_seqs, const int32_t* group_starts,
+                           int32_t num_groups, int32_t max_group_size, const int32_t* prefix_page_table,
+                           int32_t prefix_pt_stride, const int32_t* shared_lens, int32_t max_shared_len,
+                           uint32_t* flags, void* stream);
 
 /*
  * pa_gather: copy the first seq_lens[b] tokens of every request, in logical

@@ -10,7 +10,6 @@ from .paged_attention import (  # noqa: F401
     extend,
     gather,
     kv_store,
-    round_to_bf16_f64,
     token_slots,
     widen,
 )

@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
 benchmark's CPU-baseline leg import this module; the product path (the HIP
 library and its binding) never does, and this module imports nothing from it.
 
-It computes, slowly and in float64, what the pages define:
+It computes, slowly, what the pages define, in float64 by default or, with
+acc="f32", in float32 throughout (the inputs are bf16 or fp32, which float32
+holds exactly; only the arithmetic is rounded):
 
 * Pool layout -- K and V live in fixed-size pages, each page holding
   page_size token rows of [num_kv_heads, head_dim] ("NHD"): nanoSGLang README,
@@ -37,6 +39,7 @@ zero row; slots below zero in a slot mapping are padding and skipped;
 duplicate slots are rejected.
 
 bf16 arrays are carried as uint16 bit patterns and widened exactly.
+Results are returned as float64 arrays in both precisions.
 """
 from __future__ import annotations
 
@@ -57,6 +60,16 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+ACC_TYPES = {"f64": np.float64, "f32": np.float32}
+
+
+def _acc_type(acc: str):
+    """numpy type of the arithmetic: "f64" or "f32"."""
+    if acc not in ACC_TYPES:
+        raise ValueError(f"unknown accumulation precision {acc!r}")
+    return ACC_TYPES[acc]
 
 
 # --------------------------------------------------------------------------
@@ -124,13 +137,16 @@ def _softmax_rows_attend(s: np.ndarray, V: np.ndarray) -> np.ndarray:
     return np.divide(num, den, out=np.zeros_like(num), where=den > 0)
 
 
-def decode(q, k_pool, v_pool, page_table, seq_lens, scale: float, dtype: str) -> np.ndarray:
+def decode(q, k_pool, v_pool, page_table, seq_lens, scale: float, dtype: str, acc: str = "f64") -> np.ndarray:
     """One new token per request attends every key of its request.
 
     q [B, H_q, D]; returns float64 [B, H_q, D].  For request b with L_b keys
     and query head h (KV head g = h // G):  out = softmax(scale * K_g q) V_g.
+    acc: precision of the arithmetic ("f64" or "f32").
     """
-    q = widen(q, dtype)
+    at = _acc_type(acc)
+    scale = at(scale)
+    q = widen(q, dtype).astype(at)
     B, Hq, D = q.shape
     Hkv = k_pool.shape[2]
     if Hq % Hkv:
@@ -140,8 +156,8 @@ def decode(q, k_pool, v_pool, page_table, seq_lens, scale: float, dtype: str) ->
         L = int(seq_lens[b])
         if L == 0:
             continue
-        K = widen(gather(k_pool, page_table[b], L), dtype)  # [L, Hkv, D]
-        V = widen(gather(v_pool, page_table[b], L), dtype)
+        K = widen(gather(k_pool, page_table[b], L), dtype).astype(at)  # [L, Hkv, D]
+        V = widen(gather(v_pool, page_table[b], L), dtype).astype(at)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             s = scale * (K[:, g, :] @ q[b, h])
@@ -149,15 +165,18 @@ def decode(q, k_pool, v_pool, page_table, seq_lens, scale: float, dtype: str) ->
     return out
 
 
-def extend(q, q_indptr, k_pool, v_pool, page_table, seq_lens, scale: float, dtype: str) -> np.ndarray:
+def extend(q, q_indptr, k_pool, v_pool, page_table, seq_lens, scale: float, dtype: str,
+           acc: str = "f64") -> np.ndarray:
     """A chunk of n_b new tokens per request after a cached prefix.
 
     q [T_q, H_q, D] with request b's rows at q_indptr[b] .. q_indptr[b+1];
     n_b = q_indptr[b+1] - q_indptr[b], prefix p_b = seq_lens[b] - n_b.  New
     token i (absolute position p_b + i) sees keys j <= p_b + i.  Returns
-    float64 [T_q, H_q, D].
+    float64 [T_q, H_q, D].  acc: precision of the arithmetic.
     """
-    q = widen(q, dtype)
+    at = _acc_type(acc)
+    scale = at(scale)
+    q = widen(q, dtype).astype(at)
     T, Hq, D = q.shape
     Hkv = k_pool.shape[2]
     if Hq % Hkv:
@@ -172,8 +191,8 @@ def extend(q, q_indptr, k_pool, v_pool, page_table, seq_lens, scale: float, dtyp
         p = L - n
         if p < 0:
             raise ValueError("chunk longer than the sequence")
-        K = widen(gather(k_pool, page_table[b], L), dtype)
-        V = widen(gather(v_pool, page_table[b], L), dtype)
+        K = widen(gather(k_pool, page_table[b], L), dtype).astype(at)
+        V = widen(gather(v_pool, page_table[b], L), dtype).astype(at)
         i = np.arange(n)[:, None]
         j = np.arange(L)[None, :]
         mask = visible(i, j, p)  # [n, L]
@@ -237,15 +256,3 @@ def combine(o, lse, n_splits) -> np.ndarray:
         w = np.exp(l - l.max(axis=1, keepdims=True))  # [Hq, n]
         out[b] = np.einsum("hs,hsd->hd", w, o[b, :, :n, :]) / w.sum(axis=1)[:, None]
     return out
-
-
-# --------------------------------------------------------------------------
-# output formats
-# --------------------------------------------------------------------------
-def round_to_bf16_f64(x: np.ndarray) -> np.ndarray:
-    """Value of x after rounding to bfloat16 (nearest, ties to even), as
-    float64.  Used to state what a bf16 output can at best be."""
-    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = x32.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)

@@ -85,6 +85,7 @@ SIGNATURES = {
     "pa_verify_workspace_bytes": (_sz, [_i32] * 7),
     "pa_verify": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
     "pa_check_batch": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i64, _vp, _vp]),
+    "pa_check_cascade": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp]),
     "pa_gather": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
 }
 
@@ -428,7 +429,8 @@ def verify(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, max_seq
     return out
 
 
-CHECK_BITS = {1: "seq_len", 2: "q_indptr", 4: "page_id", 8: "slot_range", 16: "slot_duplicate"}
+CHECK_BITS = {1: "seq_len", 2: "q_indptr", 4: "page_id", 8: "slot_range", 16: "slot_duplicate",
+              32: "group_starts", 64: "shared_len", 128: "prefix_page"}
 
 
 def check_batch(k_pool, v_pool, page_table, seq_lens, max_seq_len, q_indptr=None, max_q_len=0, slot_mapping=None,
@@ -447,8 +449,35 @@ def check_batch(k_pool, v_pool, page_table, seq_lens, max_seq_len, q_indptr=None
                                seq_lens.numel(), int(max_seq_len), _ptr(q_indptr), int(max_q_len),
                                _ptr(slot_mapping), n_rows, _ptr(flags), _stream(stream))
     _check(st, "pa_check_batch")
+    return _read_flags(flags, stream)
+
+
+def _read_flags(flags, stream):
+    """Names of the bits set in a check's flag word, read after the check's
+    own stream has finished (it need not be the current stream)."""
+    torch = _torch()
+    (stream if stream is not None else torch.cuda.current_stream()).synchronize()
     word = int(flags.item()) & 0xFFFFFFFF
     return sorted(name for bit, name in CHECK_BITS.items() if word & bit)
+
+
+def check_cascade(k_pool, v_pool, page_table, seq_lens, group_starts, max_group_size, prefix_page_table,
+                  shared_lens, max_shared_len, stream=None):
+    """Debug check of a cascade decode's group description (group starts,
+    shared lengths, prefix pages against each request's own pages);
+    synchronises and returns the names of the violations found."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    for t, n in ((page_table, "page_table"), (seq_lens, "seq_lens"), (group_starts, "group_starts"),
+                 (prefix_page_table, "prefix_page_table"), (shared_lens, "shared_lens")):
+        _dev(t, n, torch.int32)
+    flags = torch.empty(1, dtype=torch.int32, device=k_pool.device)
+    st = load().pa_check_cascade(ctypes.byref(pool), _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                                 seq_lens.numel(), _ptr(group_starts), group_starts.numel() - 1, int(max_group_size),
+                                 _ptr(prefix_page_table), prefix_page_table.shape[1], _ptr(shared_lens),
+                                 int(max_shared_len), _ptr(flags), _stream(stream))
+    _check(st, "pa_check_cascade")
+    return _read_flags(flags, stream)
 
 
 def gather(k_pool, v_pool, page_table, seq_lens, out_offsets, max_seq_len, k_out, v_out, stream=None):

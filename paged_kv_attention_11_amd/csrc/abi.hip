@@ -142,7 +142,8 @@ size_t workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, 
 pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                          const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
                          int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
-                         void* out, void* workspace, size_t ws_bytes, pa::DecodeArgs& a) {
+                         void* out, void* workspace, size_t ws_bytes, pa::DecodeArgs& a,
+                         bool check_workspace = true) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || max_seq_len < 0 || pt_stride < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
@@ -160,8 +161,8 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
     if (!q || !page_table || !seq_lens || !out) return PA_ERR_NULL;
     if (!aligned(q, 16)) return PA_ERR_SHAPE;
     const size_t need = workspace_bytes(num_seqs, num_q_heads, pool->head_dim, max_seq_len, split);
-    if (ws_bytes < need) return PA_ERR_WORKSPACE;
-    if (S > 0 && (!workspace || !aligned(workspace, 256))) return PA_ERR_WORKSPACE;
+    if (check_workspace && ws_bytes < need) return PA_ERR_WORKSPACE;
+    if (check_workspace && S > 0 && (!workspace || !aligned(workspace, 256))) return PA_ERR_WORKSPACE;
   }
   const size_t rows = (size_t)num_seqs * num_q_heads * S;
   a.k_pool = pool->k_pool;
@@ -398,7 +399,7 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
     return PA_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int G = num_q_heads / pool->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G < 1 || G > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (max_q_len > max_seq_len) return PA_ERR_SHAPE;
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
   const int64_t qblocks = (max_q_len + 128 / G - 1) / (128 / G);
@@ -473,7 +474,7 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
     return PA_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int G = num_q_heads / pool->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G < 1 || G > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
   if ((int64_t)prefix_pt_stride * pool->page_size < max_shared_len) return PA_ERR_SHAPE;
   if (max_group_size > num_seqs) return PA_ERR_SHAPE;
@@ -608,7 +609,7 @@ pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_h
   if (st != PA_OK) return st;
   if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
   const int G = num_q_heads / pool->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G < 1 || G > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (max_q_len < 0 || max_q_len > max_seq_len) return PA_ERR_SHAPE;
   const int64_t qblocks = (max_q_len + 128 / G - 1) / (128 / G);
   if (qblocks * pool->num_kv_heads * num_seqs > (int64_t)INT_MAX) return PA_ERR_SHAPE;
@@ -667,7 +668,7 @@ pa_status pa_verify(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
     return PA_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int G = num_q_heads / pool->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G < 1 || G > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_q_len * G > 32) return PA_ERR_UNSUPPORTED;  // rows of one matrix-core tile pair
   if (max_q_len > max_seq_len) return PA_ERR_SHAPE;
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
@@ -730,6 +731,39 @@ pa_status pa_check_batch(const pa_kv_pool* pool, const int32_t* page_table, int3
   a.max_q_len = max_q_len;
   a.page_size = pool->page_size;
   return hip_status(pa::launch_check(a, (hipStream_t)stream));
+}
+
+pa_status pa_check_cascade(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                           const int32_t* seq_lens, int32_t num_seqs, const int32_t* group_starts,
+                           int32_t num_groups, int32_t max_group_size, const int32_t* prefix_page_table,
+                           int32_t prefix_pt_stride, const int32_t* shared_lens, int32_t max_shared_len,
+                           uint32_t* flags, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || pt_stride < 0 || num_groups < 0 || max_group_size < 0 || prefix_pt_stride < 0 ||
+      max_shared_len < 0)
+    return PA_ERR_SHAPE;
+  if (!flags) return PA_ERR_NULL;
+  if (!aligned(flags, 4)) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && num_groups > 0 &&
+      (!page_table || !seq_lens || !group_starts || !prefix_page_table || !shared_lens))
+    return PA_ERR_NULL;
+  pa::CascadeCheckArgs a;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.group_starts = group_starts;
+  a.prefix_page_table = prefix_page_table;
+  a.shared_lens = shared_lens;
+  a.flags = flags;
+  a.num_pages = pool->num_pages;
+  a.pt_stride = pt_stride;
+  a.prefix_pt_stride = prefix_pt_stride;
+  a.num_seqs = num_seqs;
+  a.num_groups = num_groups;
+  a.max_group_size = max_group_size;
+  a.max_shared_len = max_shared_len;
+  a.page_size = pool->page_size;
+  return hip_status(pa::launch_check_cascade(a, (hipStream_t)stream));
 }
 
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,

@@ -64,7 +64,59 @@ __global__ __launch_bounds__(kThreads) void check_slots(const CheckArgs a) {
   if (bad) atomicOr(a.flags, bad);
 }
 
+// One thread per request of a cascade decode: its group (found by binary
+// search in group_starts, which one thread checks whole), its shared length,
+// and that the pages holding its shared keys are its group's prefix pages.
+__global__ __launch_bounds__(kThreads) void check_groups(const CascadeCheckArgs a) {
+  uint32_t bad = 0;
+  const int tid = blockIdx.x * kThreads + threadIdx.x;
+  if (tid == 0) {
+    if (a.group_starts[0] != 0 || a.group_starts[a.num_groups] != a.num_seqs) bad |= PA_CHECK_GROUP_STARTS;
+    for (int j = 0; j < a.num_groups; ++j) {
+      const int n = a.group_starts[j + 1] - a.group_starts[j];
+      if (n < 0 || n > a.max_group_size) bad |= PA_CHECK_GROUP_STARTS;
+    }
+  }
+  for (int b = tid; b < a.num_seqs; b += gridDim.x * kThreads) {
+    // the last group whose start is <= b (any in-range group if the starts
+    // are broken: that is reported above)
+    int lo = 0, hi = a.num_groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.group_starts[mid] <= b) lo = mid;
+      else hi = mid - 1;
+    }
+    const int sh = a.shared_lens[b];
+    const int L = a.seq_lens[b];
+    if (sh < 0 || sh > a.max_shared_len || sh > L) bad |= PA_CHECK_SHARED_LEN;
+    // pages of the shared keys the calls would read, within both table rows
+    const int64_t keys = min(max(sh, 0), a.max_shared_len);
+    int64_t np = (keys + a.page_size - 1) / a.page_size;
+    np = min(np, (int64_t)min(a.pt_stride, a.prefix_pt_stride));
+    const int32_t* own = a.page_table + (int64_t)b * a.pt_stride;
+    const int32_t* pre = a.prefix_page_table + (int64_t)lo * a.prefix_pt_stride;
+    for (int64_t t = 0; t < np; ++t) {
+      const int32_t pg = pre[t];
+      if (pg < 0 || pg >= a.num_pages || pg != own[t]) {
+        bad |= PA_CHECK_PREFIX_PAGE;
+        break;
+      }
+    }
+  }
+  if (bad) atomicOr(a.flags, bad);
+}
+
 }  // namespace
+
+hipError_t launch_check_cascade(const CascadeCheckArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_flags, dim3(1), dim3(64), 0, stream, a.flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_seqs <= 0 || a.num_groups <= 0) return e;
+  const int64_t want = (a.num_seqs + kThreads - 1) / kThreads;
+  const int64_t blocks = want < 1024 ? want : 1024;
+  hipLaunchKernelGGL(check_groups, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(clear_flags, dim3(1), dim3(64), 0, stream, a.flags);

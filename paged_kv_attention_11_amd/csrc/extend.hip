@@ -20,7 +20,7 @@
 // Design (FlashAttention-2 style tiling written for the CDNA4 matrix core):
 //  * Work-group = 4 waves = 128 query rows = (128 / G) tokens (or group
 //    members) x all G query heads of one KV head, so every K/V tile staged in
-//    LDS serves G heads.
+//    LDS serves G heads (for G = 3, 5, 6, 7 the last 128 mod G rows idle).
 //  * Per wave: 32 query rows.  Scores are computed transposed,
 //    S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in
 //    registers), so each lane owns one query row of the score tile and the
@@ -114,6 +114,9 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   const int half = lane >> 5;
   const int row = wave * 32 + col;  // rows are (head, token/member) with token fastest
   const int hq = row / TOK;
+  // when G does not divide the work-group's rows, the last G * TOK .. kRows - 1
+  // are padding (no query head): never loaded, never written
+  const bool head_ok = hq < G;
 
   // ---- extend: the requests that run work-groups here (more than one row,
   // or one when single rows are not skipped) first, in order of decreasing
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     k_begin = 0;
     k_end = prefix + min(i0 + TOK, n);  // keys this block can see
     const int ti = i0 + (row % TOK);
-    qvalid = ti < n;
+    qvalid = head_ok && ti < n;
     q_row = r0 + ti;
     vis_lim = prefix + (qvalid ? ti : (n - 1));  // padding rows mask like the last token
     min_vis = prefix + i0;
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     const int m0 = rb * TOK;
     if (m0 >= gsize) break;
     const int mi = m0 + (row % TOK);
-    qvalid = mi < gsize;
+    qvalid = head_ok && mi < gsize;
     q_row = m_begin + (qvalid ? mi : m0);
     // clamped so that no key beyond the group's page-table rows is addressed
     const int shared = qvalid ? min(p.seq_lens[q_row], p.max_keys) : 0;
@@ -654,7 +657,11 @@ hipError_t launch_d(const ExtendArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
     case 1: return launch_g<D, 1, PREFIX>(a, stream);
     case 2: return launch_g<D, 2, PREFIX>(a, stream);
+    case 3: return launch_g<D, 3, PREFIX>(a, stream);
     case 4: return launch_g<D, 4, PREFIX>(a, stream);
+    case 5: return launch_g<D, 5, PREFIX>(a, stream);
+    case 6: return launch_g<D, 6, PREFIX>(a, stream);
+    case 7: return launch_g<D, 7, PREFIX>(a, stream);
     case 8: return launch_g<D, 8, PREFIX>(a, stream);
     default: return hipErrorInvalidValue;
   }

@@ -178,6 +178,23 @@ struct CheckArgs {
   int32_t page_size;
 };
 
+struct CascadeCheckArgs {
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* group_starts;
+  const int32_t* prefix_page_table;
+  const int32_t* shared_lens;
+  uint32_t* flags;
+  int64_t num_pages;
+  int32_t pt_stride;
+  int32_t prefix_pt_stride;
+  int32_t num_seqs;
+  int32_t num_groups;
+  int32_t max_group_size;
+  int32_t max_shared_len;
+  int32_t page_size;
+};
+
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_rope_store(const RopeArgs& a, hipStream_t stream);
@@ -190,5 +207,6 @@ hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const ExtendArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
+hipError_t launch_check_cascade(const CascadeCheckArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -390,7 +390,11 @@ hipError_t launch_d(const VerifyArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
     case 1: return launch_g<D, 1>(a, stream);
     case 2: return launch_g<D, 2>(a, stream);
+    case 3: return launch_g<D, 3>(a, stream);
     case 4: return launch_g<D, 4>(a, stream);
+    case 5: return launch_g<D, 5>(a, stream);
+    case 6: return launch_g<D, 6>(a, stream);
+    case 7: return launch_g<D, 7>(a, stream);
     case 8: return launch_g<D, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }

@@ -62,6 +62,18 @@ def named(name, poison="nan"):
     return wl, dw
 
 
+@functools.lru_cache(maxsize=4)
+def oracle_whole(name):
+    """The oracle's output for every request of a named workload (decode
+    workloads: oracle.decode; workloads with chunks: oracle.extend), computed
+    once per test session."""
+    wl = W.make(name, poison="nan")
+    kp, vp = stored_oracle_pools(wl)
+    if wl.kind == "decode":
+        return oracle.decode(wl.q, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    return oracle.extend(wl.q, wl.q_indptr, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+
+
 def gpu_decode(wl, dw, split=0, out=None):
     o = pa().decode(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, wl.scale,
                     out=out, split_tokens=split)

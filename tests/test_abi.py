@@ -178,7 +178,7 @@ def test_heads_per_block_invalid_arguments():
 def test_extend_validation():
     p = pool()
     assert extend(pool(dtype=0)) == DTYPE
-    assert extend(p, Hq=24) == UNSUP  # group 3
+    assert extend(p, Hq=72) == UNSUP  # group 9
     assert extend(p, Hq=30) == SHAPE
     assert extend(p, qmax=2000) == SHAPE  # longer than max_seq_len
     assert extend(p, stride=8) == SHAPE
@@ -203,7 +203,7 @@ def test_cascade_validation(fn):
     p = pool()
     cascade = lambda *a, **k: globals()["cascade"](*a, fn=fn, **k)
     assert cascade(pool(dtype=0)) == DTYPE
-    assert cascade(p, Hq=24) == UNSUP  # group 3 has no matrix-core tile
+    assert cascade(p, Hq=72) == UNSUP  # group 9
     assert cascade(p, Hq=30) == SHAPE
     assert cascade(p, pstride=7) == SHAPE  # 7 * 16 < 128 shared keys
     assert cascade(p, stride=10) == SHAPE
@@ -286,7 +286,7 @@ def mixed(p, q=FAKE, Hq=32, qi=FAKE, pt=FAKE, stride=64, sl=FAKE, B=4, qmax=128,
 def test_mixed_validation():
     p = pool()
     assert mixed(pool(dtype=0)) == DTYPE
-    assert mixed(p, Hq=24) == UNSUP  # group 3: no matrix-core tile
+    assert mixed(p, Hq=72) == UNSUP  # group 9
     assert mixed(p, Hq=30) == SHAPE
     assert mixed(p, qmax=2000) == SHAPE
     assert mixed(p, qmax=-1) == SHAPE
@@ -309,7 +309,8 @@ def verify(p, q=FAKE, Hq=32, qi=FAKE, pt=FAKE, stride=64, sl=FAKE, B=4, qmax=6, 
 def test_verify_validation():
     p = pool()
     assert verify(pool(dtype=0)) == DTYPE
-    assert verify(p, Hq=24) == UNSUP
+    assert verify(p, Hq=72) == UNSUP  # group 9
+    assert verify(p, Hq=56, qmax=5) == UNSUP  # 5 rows x 7 heads > 32
     assert verify(p, qmax=9) == UNSUP  # 9 rows x 4 heads > 32
     assert verify(p, Hq=64, qmax=5) == UNSUP  # 5 x 8 > 32
     assert verify(p, Hq=30) == SHAPE
@@ -344,6 +345,21 @@ def test_check_batch_validation():
     assert call(sl=0) == NULL
     assert call(n=4) == NULL  # rows without a slot mapping
     assert call(B=-1) == SHAPE
+    assert call(flags=FAKE + 2) == SHAPE
+
+
+def test_check_cascade_validation():
+    lib = pa.load()
+    p = pool()
+    call = lambda pt=FAKE, sl=FAKE, B=4, gs=FAKE, ng=2, gmax=2, ppt=FAKE, shl=FAKE, msh=64, flags=FAKE: \
+        lib.pa_check_cascade(ctypes.byref(p), pt, 64, sl, B, gs, ng, gmax, ppt, 8, shl, msh, flags, None)
+    assert call(flags=0) == NULL
+    assert call(gs=0) == NULL
+    assert call(ppt=0) == NULL
+    assert call(shl=0) == NULL
+    assert call(B=-1) == SHAPE
+    assert call(ng=-1) == SHAPE
+    assert call(msh=-1) == SHAPE
     assert call(flags=FAKE + 2) == SHAPE
 
 

@@ -8,8 +8,8 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import (assert_close, bits, f64, fresh, gpu_cascade, gpu_decode, named, stored_oracle_pools,
-                         torch)
+from gpu_helpers import (assert_close, bits, f64, fresh, gpu_cascade, gpu_decode, named, oracle_whole,
+                         stored_oracle_pools, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,17 +25,15 @@ def oracle_decode(wl, seqs=None):
 
 
 def test_cascade_matches_oracle_on_the_qwen3_8b_radix_workload():
+    """Every element of all 256 requests against the oracle, and against the
+    plain decode of the same inputs."""
     name = "qwen3_8b_radix"
     banner(f"cascade {name}")
     wl, dw = named(name)
     out = f64(gpu_cascade(wl, dw))
-    # two whole sharing groups, plus the shortest and longest requests
-    order = np.argsort(wl.seq_lens)
-    seqs = sorted(set(range(32)) | set(order[:3].tolist()) | set(order[-3:].tolist()))
-    err = assert_close(out[seqs], oracle_decode(wl, seqs), f"cascade {name}")
-    # every request against the plain decode of the same inputs
+    err = assert_close(out, oracle_whole(name), f"cascade {name}")
     assert_close(out, f64(gpu_decode(wl, dw)), f"cascade vs decode {name}")
-    print(f"[result] cascade {name}: {len(seqs)} requests vs oracle, max abs err {err:.3g}", flush=True)
+    print(f"[result] cascade {name}: all {wl.num_seqs} requests vs oracle, max abs err {err:.3g}", flush=True)
 
 
 CASCADE_SWEEP = [
@@ -51,6 +49,11 @@ CASCADE_SWEEP = [
     ([3000, 2500, 2900, 1200], 8, 2, 128, 1, (4, 2048), 0, 0),
     ([1000, 1000, 1000], 64, 8, 128, 256, (3, 3), 0, 0),               # largest page
     ([0, 5, 0, 40, 33], 8, 2, 128, 16, (5, 2), 0, 0),                   # empty requests in a group
+    ([300, 500, 640, 128, 200, 610, 333], 14, 2, 64, 16, (4, 8), 0, 0),  # group 7 (Qwen2.5-0.5B heads)
+    (list(range(100, 140)), 14, 2, 64, 16, (20, 6), 64, 64),            # group 7: 20 members, two row blocks
+    ([700, 1200, 1500, 900, 1800], 40, 8, 128, 16, (5, 32), 0, 0),      # group 5
+    ([700, 1200, 1500, 900], 24, 8, 128, 16, (2, 32), 0, 0),            # group 3
+    ([700, 1200, 1500, 900], 48, 8, 128, 16, (4, 32), 128, 0),          # group 6
 ]
 
 

@@ -57,3 +57,35 @@ def test_each_violation_sets_its_bit():
     assert check(wl, dw, slots=sm) == ["slot_duplicate"]
     sm = wl.slot_mapping.copy(); sm[10] = -1; sm[50] = -1  # padding twice is fine
     assert check(wl, dw, slots=sm) == []
+
+
+def test_cascade_description_checks():
+    banner("check: cascade group description")
+    T = torch()
+    wl = W.make_custom([300, 200, 90, 400, 129, 40], 8, 2, 128, 16, dtype="bf16", radix=(3, 8), seed=801)
+    dw = fresh(wl)
+    starts, ppt, shl = wl.cascade_inputs()
+    dev = lambda x: T.from_numpy(np.ascontiguousarray(x, np.int32)).cuda()
+    gmax = int(np.diff(starts).max())
+    msh = int(shl.max())
+
+    def run(starts=starts, ppt=ppt, shl=shl, gmax=gmax, msh=msh):
+        return pa().check_cascade(dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, dev(starts), gmax, dev(ppt),
+                                  dev(shl), msh)
+
+    assert run() == []
+    s2 = starts.copy(); s2[-1] -= 1
+    assert run(starts=s2) == ["group_starts"]
+    assert run(gmax=gmax - 1) == ["group_starts"]
+    sh2 = shl.copy(); sh2[0] = msh + 16
+    assert "shared_len" in run(shl=sh2)
+    assert run(msh=msh - 1) == ["shared_len"]
+    sh2 = shl.copy(); sh2[1] = -1
+    assert run(shl=sh2) == ["shared_len"]
+    p2 = ppt.copy(); p2[0, 0] = (p2[0, 0] + 1) % wl.num_pages  # not request 0's first page any more
+    assert run(ppt=p2) == ["prefix_page"]
+    p2 = ppt.copy(); p2[1, 0] = wl.num_pages
+    assert run(ppt=p2) == ["prefix_page"]
+    # a request that shares nothing may sit in a group of its own
+    sh2 = shl.copy(); sh2[2] = 0
+    assert run(shl=sh2) == []

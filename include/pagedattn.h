@@ -76,7 +76,8 @@
  *     q_indptr) are a caller contract and are not checked: page ids must be in
  *     [0, num_pages), seq_lens in [0, max_seq_len], slots in
  *     [0, num_pages * page_size) or negative (skip), distinct.
- *   - The library keeps no state between calls and is thread-safe.
+ *   - The library keeps no state between calls and is thread-safe, except
+ *     for the static scratch buffer of pa_decode_noalloc (see there).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -95,7 +96,8 @@ typedef enum {
   PA_ERR_DTYPE = 3,       /* unknown dtype, or a dtype this call does not take  */
   PA_ERR_UNSUPPORTED = 4, /* valid, but head_dim / group / page size not built  */
   PA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned         */
-  PA_ERR_HIP = 6          /* a HIP runtime call reported an error               */
+  PA_ERR_HIP = 6,         /* a HIP runtime call reported an error               */
+  PA_ERR_SCRATCH = 7      /* pa_decode_noalloc: more than the static scratch    */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -216,6 +218,33 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                     const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
                     int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_noalloc: pa_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, result and kernels as pa_decode, without the
+ * workspace: the split partials go to a buffer of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds in static device memory,
+ * one copy per GPU, kept from the loading of the library's code on that GPU
+ * until the process ends.  The call itself allocates and frees nothing.
+ *   - A call whose partials would need more than PA_NOALLOC_SCRATCH_BYTES
+ *     (pa_decode_workspace_bytes(...) for the same sizes) returns
+ *     PA_ERR_SCRATCH and launches nothing.  The Qwen3-8B-shaped batch of 256
+ *     requests of up to 8192 keys needs about 32 MiB.
+ *   - The buffer needs no initialisation and keeps whatever the last call
+ *     left in it.
+ *   - All calls on one GPU share its buffer: two calls that can overlap on
+ *     one GPU (other streams, other host threads) race and give wrong rows.
+ *     Serialise them, or use pa_decode with a workspace of each caller's own.
+ *   - The stream must belong to the current device (PA_ERR_UNSUPPORTED
+ *     otherwise); the buffer's address on a device is looked up on the first
+ *     call made there.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, float scale, int32_t split_tokens,
+                            void* out, void* stream);
 
 /*
  * The two stages of pa_decode, callable one at a time (same arguments).

@@ -20,7 +20,7 @@ from pathlib import Path
 from typing import Optional
 
 __all__ = [
-    "PagedAttnError", "library_path", "load", "version", "kv_store", "decode", "decode_partial",
+    "PagedAttnError", "library_path", "load", "version", "kv_store", "decode", "decode_noalloc", "decode_partial",
     "decode_combine", "decode_split_tokens", "decode_heads_per_block", "decode_workspace_bytes", "extend", "gather",
 ]
 
@@ -29,7 +29,7 @@ _LIB_NAME = "libpagedattn.so"
 
 PA_F32, PA_BF16 = 0, 1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
-                4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+                4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_SCRATCH"}
 
 
 class PagedAttnError(RuntimeError):
@@ -70,6 +70,7 @@ SIGNATURES = {
     "pa_decode_heads_per_block": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
+    "pa_decode_noalloc": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp]),
     "pa_decode_partial": (_i32, _DECODE_ARGS),
     "pa_decode_combine": (_i32, _DECODE_ARGS),
     "pa_extend": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp]),
@@ -266,6 +267,29 @@ def decode(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out=None
     """Paged decode attention: q [B, H_q, D] -> out [B, H_q, D] (pool dtype)."""
     return _decode_call("pa_decode", q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out,
                         workspace, split_tokens, stream)
+
+
+def decode_noalloc(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out, split_tokens=0, stream=None):
+    """decode(...) without a workspace: the library's static scratch buffer
+    holds the split partials, and nothing is allocated (so `out` must be
+    given).  Calls that can overlap on one GPU race on that buffer."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool)
+    _dev(q, "q", k_pool.dtype)
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if out is None:
+        raise ValueError("decode_noalloc allocates nothing: pass `out`")
+    _dev(out, "out", q.dtype)
+    if q.dim() != 3 or q.shape[2] != k_pool.shape[3] or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_dim]")
+    if page_table.dim() != 2 or page_table.shape[0] != q.shape[0] or seq_lens.numel() != q.shape[0]:
+        raise ValueError("page_table [num_seqs, stride] and seq_lens [num_seqs] must match q")
+    st = load().pa_decode_noalloc(ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(page_table), page_table.shape[1],
+                                  _ptr(seq_lens), q.shape[0], int(max_seq_len), float(scale), int(split_tokens),
+                                  _ptr(out), _stream(stream))
+    _check(st, "pa_decode_noalloc")
+    return out
 
 
 def decode_partial(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, out, workspace,

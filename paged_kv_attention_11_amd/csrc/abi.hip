@@ -1,13 +1,49 @@
 // C ABI of the paged-attention library: host-side validation and dispatch.
 // Every argument is checked before the first HIP call; a call that fails
-// validation launches nothing.  The library allocates nothing, never
-// synchronises, and keeps no state.
+// validation launches nothing.  The library allocates nothing and never
+// synchronises; its only state is the per-device address of the static
+// scratch buffer of pa_decode_noalloc.
 #include <limits.h>
+
+#include <mutex>
 
 #include "pagedattn.h"
 #include "internal.h"
 
+// Scratch memory of pa_decode_noalloc, for callers that cannot allocate
+// device memory.  Every GPU the library runs on holds its own copy of the
+// array from the moment the code object is loaded there until the process
+// ends.  In host code `scratch` is only a stand-in for the symbol: its device
+// address is looked up once per device (scratch_address) and only that
+// address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (which must be the
+// device of `stream`), looked up on the first call on that device.
+pa_status scratch_address(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return PA_ERR_HIP;
+    if (sdev != dev) return PA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
 
 using pa::kMaxGroup;
 using pa::kMaxSplitTokens;
@@ -273,6 +309,7 @@ const char* pa_status_string(int32_t s) {
     case PA_ERR_UNSUPPORTED: return "unsupported head_dim, group size or page size";
     case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_SCRATCH: return "call needs more than the library's static scratch buffer holds";
     default: return "unknown status";
   }
 }
@@ -384,6 +421,29 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   st = enqueue_partial(a, (hipStream_t)stream);
   if (st != PA_OK) return st;
   // one piece per request: the partial kernel wrote every row (zero rows too)
+  if (a.max_splits <= 1) return PA_OK;
+  return hip_status(pa::launch_decode_combine(a, (hipStream_t)stream));
+}
+
+pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* page_table,
+                            int32_t pt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                            float scale, int32_t split_tokens, void* out, void* stream) {
+  // host-side checks first: the sizes, then whether the partials fit
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs, max_seq_len,
+                                scale, split_tokens, out, nullptr, 0, a, /*check_workspace=*/false);
+  if (st != PA_OK || num_seqs == 0) return st;
+  const size_t need = workspace_bytes(num_seqs, num_q_heads, pool->head_dim, max_seq_len, a.split_tokens);
+  if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address((hipStream_t)stream, &ws);
+  if (st != PA_OK) return st;
+  // the same plan and kernels as pa_decode, on the static buffer
+  st = prepare_decode(pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs, max_seq_len, scale,
+                      split_tokens, out, ws, PA_NOALLOC_SCRATCH_BYTES, a);
+  if (st != PA_OK) return st;
+  st = enqueue_partial(a, (hipStream_t)stream);
+  if (st != PA_OK) return st;
   if (a.max_splits <= 1) return PA_OK;
   return hip_status(pa::launch_decode_combine(a, (hipStream_t)stream));
 }

@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--path", choices=["cascade", "plain"], default="cascade",
                     help="decode path of the timed step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU leg")
+    ap.add_argument("--only", choices=["extend", "verify", "rope"],
+                    help="time only this call (for profiler runs) and print its object")
     ap.add_argument("--copy-only", action="store_true",
                     help="only the plain-copy calibration (for hardware-counter scaling runs)")
     return ap.parse_args()
@@ -351,6 +353,36 @@ def bench_mixed(pa, W, torch, np, stream, iters):
             "tokens_per_s": round(int(mw.q_indptr[-1]) / (replay * 1e-3), 1)}
 
 
+def bench_extend(pa, W, torch, np, stream, iters, warmup=3):
+    """The extend call on the Qwen3-8B-shaped chunked-prefill workload, with
+    its matrix-core roofline (algorithmic FLOPs: causal-visible pairs only)."""
+    ew = W.make("qwen3_8b_extend")
+    edw = W.to_device(ew)
+    eout = torch.empty_like(edw.q)
+    pa.kv_store(edw.k_pool, edw.v_pool, edw.k_new, edw.v_new, edw.slot_mapping)
+
+    def ext():
+        pa.extend(edw.q, edw.q_indptr, edw.k_pool, edw.v_pool, edw.page_table, edw.seq_lens, ew.max_q_len,
+                  ew.max_seq_len, ew.scale, out=eout)
+
+    for _ in range(warmup):
+        ext()
+    ems = _time(torch, stream, ext, iters)
+    n = ew.n_new.astype(np.int64)
+    p = (ew.seq_lens - ew.n_new).astype(np.int64)
+    flops = 4 * ew.head_dim * ew.num_q_heads * int(np.sum(n * p + n * (n + 1) // 2))
+    tf = flops / (ems * 1e-3) / 1e12
+    return {
+        "workload": "qwen3_8b_extend",
+        "description": W.DESCRIPTIONS["qwen3_8b_extend"],
+        "kernel_us": round(ems * 1e3, 2),
+        "tokens_per_s": round(int(n.sum()) / (ems * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": read_traffic("extend"), "algorithmic_flops_per_launch": flops},
+    }
+
+
 def cpu_baseline(wl, target_s):
     """The oracle, as it stands, in its float32 arithmetic mode (a plain CPU
     fp32 implementation: gather the pages, then naive softmax attention per
@@ -422,6 +454,12 @@ def main():
                                                "bytes_read_per_launch": nread,
                                                "bytes_written_per_launch": nread,
                                                "launch_ms": round(ms, 4)}}), flush=True)
+        return
+
+    if args.only:
+        stream = torch.cuda.current_stream()
+        fn = {"extend": bench_extend, "verify": bench_verify, "rope": bench_rope}[args.only]
+        print(json.dumps({args.only: fn(pa, W, torch, np, stream, args.steps)}), flush=True)
         return
 
     # ---------------- decode step
@@ -662,40 +700,8 @@ def main():
 
     # ---------------- extend (chunked prefill on the same head shape)
     if not args.no_extend:
-        ew = W.make("qwen3_8b_extend")
-        edw = W.to_device(ew)
-        eout = torch.empty_like(edw.q)
-        pa.kv_store(edw.k_pool, edw.v_pool, edw.k_new, edw.v_new, edw.slot_mapping)
-
-        def ext():
-            pa.extend(edw.q, edw.q_indptr, edw.k_pool, edw.v_pool, edw.page_table, edw.seq_lens, ew.max_q_len,
-                      ew.max_seq_len, ew.scale, out=eout)
-
-        for _ in range(max(3, args.warmup // 2)):
-            ext()
-        torch.cuda.synchronize()
-        es, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ksteps = max(5, args.steps // 2)
-        es.record(stream)
-        for _ in range(ksteps):
-            ext()
-        ee.record(stream)
-        torch.cuda.synchronize()
-        ems = es.elapsed_time(ee) / ksteps
-        n = ew.n_new.astype(np.int64)
-        p = (ew.seq_lens - ew.n_new).astype(np.int64)
-        flops = 4 * ew.head_dim * ew.num_q_heads * int(np.sum(n * p + n * (n + 1) // 2))
-        tf = flops / (ems * 1e-3) / 1e12
-        result["extend"] = {
-            "workload": "qwen3_8b_extend",
-            "description": W.DESCRIPTIONS["qwen3_8b_extend"],
-            "kernel_us": round(ems * 1e3, 2),
-            "tokens_per_s": round(int(n.sum()) / (ems * 1e-3), 1),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                         "traffic": read_traffic("extend"), "algorithmic_flops_per_launch": flops},
-        }
-        log(f"extend: {ems * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        result["extend"] = bench_extend(pa, W, torch, np, stream, max(5, args.steps // 2), max(3, args.warmup // 2))
+        log(f"extend: {result['extend']['kernel_us']} us, {result['extend']['roofline']['achieved']} TFLOP/s")
 
     # ---------------- the other decode configurations (plain decode, one call)
     if not args.no_extend:

@@ -274,14 +274,34 @@ pa_status pa_decode_combine(const pa_kv_pool* pool, const void* q, int32_t num_q
  *   q, out     [q_indptr[num_seqs], num_q_heads, head_dim], bf16, 16-byte
  *              aligned; q_indptr int32 [num_seqs + 1], non-decreasing
  *   max_q_len  host-side upper bound of n_b; max_seq_len of seq_lens.
- * bf16 pools only, head_dim 128 or 64, group size 1 .. 8.  Scores and
- * the output are accumulated in fp32; softmax weights are rounded to bf16
- * before the weighted sum of V (matrix-core inputs).
+ *   split_tokens
+ *              keys per piece when the keys are split: 0 = the automatic
+ *              choice (pa_extend_workspace_bytes tells whether it splits),
+ *              else a multiple of 64; a value >= max_seq_len means no split.
+ *              The automatic plan splits only batches with few work items
+ *              (fewer than 1024 blocks of 128 / G tokens x KV heads x
+ *              requests) and long keys: a handful of requests whose chunks
+ *              attend long cached prefixes.
+ *   workspace  pa_extend_workspace_bytes(...) bytes, 256-byte aligned, when
+ *              the keys are split (NULL and 0 bytes allowed otherwise).
+ *              Layout: fp32 partial outputs [num_seqs * max_q_len,
+ *              num_q_heads, NP, head_dim] (row r of the first axis: query
+ *              row r), then (256-byte aligned) fp32 log2-sum-exp
+ *              [num_seqs * max_q_len, num_q_heads, NP],
+ *              NP = ceil(max_seq_len / split).  Clobbered; no initialisation.
+ * With split keys a second kernel merges the pieces of each row by
+ * log-sum-exp weights (each piece a row reads holds at least one key it sees).
+ * bf16 pools only, head_dim 128 or 64, group size 1 .. 8.  Scores and the
+ * output are accumulated in fp32; softmax weights are rounded to bf16 before
+ * the weighted sum of V (matrix-core inputs).
  */
+size_t pa_extend_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t split_tokens);
 pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                     const int32_t* q_indptr, const int32_t* page_table, int32_t pt_stride,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t max_q_len,
-                    int32_t max_seq_len, float scale, void* out, void* stream);
+                    int32_t max_seq_len, float scale, int32_t split_tokens, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Cascade (prefix-aware) decode.  The requests are cut into consecutive

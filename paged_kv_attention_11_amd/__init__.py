@@ -21,7 +21,8 @@ from typing import Optional
 
 __all__ = [
     "PagedAttnError", "library_path", "load", "version", "kv_store", "decode", "decode_noalloc", "decode_partial",
-    "decode_combine", "decode_split_tokens", "decode_heads_per_block", "decode_workspace_bytes", "extend", "gather",
+    "decode_combine", "decode_split_tokens", "decode_heads_per_block", "decode_workspace_bytes", "extend",
+    "extend_workspace_bytes", "gather",
 ]
 
 _PKG = Path(__file__).resolve().parent
@@ -73,7 +74,8 @@ SIGNATURES = {
     "pa_decode_noalloc": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp]),
     "pa_decode_partial": (_i32, _DECODE_ARGS),
     "pa_decode_combine": (_i32, _DECODE_ARGS),
-    "pa_extend": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp]),
+    "pa_extend_workspace_bytes": (_sz, [_i32] * 7),
+    "pa_extend": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
     "pa_cascade_piece_keys": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_cascade_workspace_bytes": (_sz, [_i32] * 10),
     "pa_decode_cascade": (_i32, _CASCADE_ARGS),
@@ -306,9 +308,17 @@ def decode_combine(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, scale, 
                         out, workspace, split_tokens, stream)
 
 
+def extend_workspace_bytes(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                           split_tokens=0) -> int:
+    """Workspace of extend(...) for these sizes: 0 when the keys are not split."""
+    return load().pa_extend_workspace_bytes(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                            split_tokens)
+
+
 def extend(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, max_seq_len, scale, out=None,
-           stream=None):
-    """Paged extend attention: q [T_q, H_q, D] bf16 -> out [T_q, H_q, D] bf16."""
+           stream=None, split_tokens=0, workspace=None):
+    """Paged extend attention: q [T_q, H_q, D] bf16 -> out [T_q, H_q, D] bf16.
+    split_tokens: keys per piece (0 = automatic; >= max_seq_len: no split)."""
     torch = _torch()
     pool = make_pool(k_pool, v_pool)
     _dev(q, "q", torch.bfloat16)
@@ -323,9 +333,16 @@ def extend(q, q_indptr, k_pool, v_pool, page_table, seq_lens, max_q_len, max_seq
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
+    if workspace is None:
+        nbytes = extend_workspace_bytes(B, int(max_q_len), q.shape[1], k_pool.shape[2], k_pool.shape[3],
+                                        int(max_seq_len), int(split_tokens))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().pa_extend(ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(q_indptr), _ptr(page_table),
                           page_table.shape[1], _ptr(seq_lens), B, int(max_q_len), int(max_seq_len),
-                          float(scale), _ptr(out), _stream(stream))
+                          float(scale), int(split_tokens), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_extend")
     return out
 

@@ -5,6 +5,7 @@
 // scratch buffer of pa_decode_noalloc.
 #include <limits.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "pagedattn.h"
@@ -294,6 +295,42 @@ size_t cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t he
   return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float)) + plan_bytes(num_seqs, S);
 }
 
+// Split extend.  The extend kernel's items are (token block, request, KV
+// head); a batch with fewer than kExtendTargetItems of them (a few requests
+// whose chunks attend long cached prefixes) leaves most of the chip idle, so
+// the automatic plan also cuts the keys into pieces, merged afterwards by a
+// combine kernel: enough pieces to reach the target, each at least
+// kExtendMinPiece keys (a shorter piece pays its prologue for too few tiles).
+constexpr int64_t kExtendTargetItems = 1024;  // two rounds of two work-groups per compute unit
+constexpr int kExtendMinPiece = 512;
+constexpr int kExtendTile = 64;
+
+// Keys per piece for these sizes: 0 = not split (one piece), -1 = invalid
+// split_tokens.  An explicit split_tokens (a multiple of 64) is taken as is;
+// one at or above max_seq_len means no split.
+int32_t resolve_extend_split(int32_t split_tokens, int32_t num_seqs, int32_t max_q_len, int G, int32_t num_kv_heads,
+                             int32_t max_seq_len) {
+  if (split_tokens < 0 || split_tokens % kExtendTile != 0) return -1;
+  if (split_tokens > 0) return split_tokens >= max_seq_len ? 0 : split_tokens;
+  const int64_t tok = 128 / G;
+  const int64_t items = (max_q_len + tok - 1) / tok * (int64_t)num_kv_heads * num_seqs;
+  if (items <= 0 || items >= kExtendTargetItems || max_seq_len < 2 * kExtendMinPiece) return 0;
+  int64_t np = (kExtendTargetItems + items - 1) / items;
+  np = std::min<int64_t>(np, max_seq_len / kExtendMinPiece);
+  if (np <= 1) return 0;
+  int64_t split = (max_seq_len + np - 1) / np;
+  split = (split + kExtendTile - 1) / kExtendTile * kExtendTile;
+  return split >= max_seq_len ? 0 : (int32_t)split;
+}
+
+size_t extend_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim,
+                              int32_t max_seq_len, int32_t split) {
+  if (split <= 0) return 0;
+  const int64_t NP = (max_seq_len + split - 1) / split;
+  const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * NP;
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -448,10 +485,21 @@ pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, int32_t num_q
   return hip_status(pa::launch_decode_combine(a, (hipStream_t)stream));
 }
 
+size_t pa_extend_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t split_tokens) {
+  if (num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int32_t split =
+      resolve_extend_split(split_tokens, num_seqs, max_q_len, num_q_heads / num_kv_heads, num_kv_heads, max_seq_len);
+  if (split < 0) return 0;
+  return extend_workspace_bytes(num_seqs, max_q_len, num_q_heads, head_dim, max_seq_len, split);
+}
+
 pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, const int32_t* q_indptr,
                     const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
-                    int32_t num_seqs, int32_t max_q_len, int32_t max_seq_len, float scale, void* out,
-                    void* stream) {
+                    int32_t num_seqs, int32_t max_q_len, int32_t max_seq_len, float scale, int32_t split_tokens,
+                    void* out, void* workspace, size_t workspace_bytes_, void* stream) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
@@ -462,11 +510,17 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   if (G < 1 || G > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (max_q_len > max_seq_len) return PA_ERR_SHAPE;
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
+  const int32_t split = resolve_extend_split(split_tokens, num_seqs, max_q_len, G, pool->num_kv_heads, max_seq_len);
+  if (split < 0) return PA_ERR_SHAPE;
+  const int64_t NP = split ? (max_seq_len + split - 1) / split : 1;
   const int64_t qblocks = (max_q_len + 128 / G - 1) / (128 / G);
-  if (qblocks * pool->num_kv_heads * num_seqs > (int64_t)INT_MAX) return PA_ERR_SHAPE;
+  if (qblocks * NP * pool->num_kv_heads * num_seqs > (int64_t)INT_MAX) return PA_ERR_SHAPE;
+  if ((int64_t)num_seqs * max_q_len * num_q_heads * NP > (int64_t)INT_MAX) return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!q || !q_indptr || !page_table || !seq_lens || !out) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16)) return PA_ERR_SHAPE;
+  const size_t need = extend_workspace_bytes(num_seqs, max_q_len, num_q_heads, pool->head_dim, max_seq_len, split);
+  if (NP > 1 && (workspace_bytes_ < need || !workspace || !aligned(workspace, 256))) return PA_ERR_WORKSPACE;
   pa::ExtendArgs a = {};
   a.k_pool = pool->k_pool;
   a.v_pool = pool->v_pool;
@@ -482,6 +536,13 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   a.head_dim = pool->head_dim;
   a.log2_page = ilog2(pool->page_size);
   a.max_q_len = max_q_len;
+  a.num_pieces = (int32_t)NP;
+  a.piece_keys = NP > 1 ? split : 0;
+  if (NP > 1) {
+    const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * NP;
+    a.o_part = (float*)workspace;
+    a.lse = (float*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float)));
+  }
   a.scale_log2 = scale * kLog2e;
   return hip_status(pa::launch_extend(a, (hipStream_t)stream));
 }
@@ -698,6 +759,7 @@ pa_status pa_attend_mixed(const pa_kv_pool* pool, const void* q, int32_t num_q_h
     e.head_dim = pool->head_dim;
     e.log2_page = ilog2(pool->page_size);
     e.max_q_len = max_q_len;
+    e.num_pieces = 1;
     e.skip_single = 1;
     e.scale_log2 = scale * kLog2e;
     st = hip_status(pa::launch_extend(e, hs));

@@ -79,9 +79,10 @@ __device__ __forceinline__ int shfl_xor_i(int x, int mask) {
   return __builtin_amdgcn_ds_bpermute((__lane_id() ^ mask) << 2, x);
 }
 
-// PREFIX = false: extend (chunk of new tokens, causal after the prefix).
+// PREFIX = false: extend (chunk of new tokens, causal after the prefix);
+//   SPLIT = true: its keys cut into pieces, partials to the workspace.
 // PREFIX = true:  shared-prefix pass of the cascade decode.
-template <int D, int G, bool PREFIX>
+template <int D, int G, bool PREFIX, bool SPLIT = false>
 __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(const ExtendArgs p) {
   using C = ExtCfg<D>;
   using SH = Shape<PREFIX>;
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   const int32_t* pt;
   if constexpr (!PREFIX) {
     const int qblocks = (p.max_q_len + TOK - 1) / TOK;
-    const int total = qblocks * p.num_kv_heads * p.num_seqs;
+    const int NP = SPLIT ? p.num_pieces : 1;  // key pieces per block
+    const int total = qblocks * NP * p.num_kv_heads * p.num_seqs;
     const int q8 = total / 8, r8 = total % 8;
     const int nx = q8 + (xcd < r8 ? 1 : 0);
     const int start = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
@@ -211,6 +213,10 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     int bid = start + within;
     const int qb = qblocks - 1 - (bid % qblocks);
     bid /= qblocks;
+    if constexpr (SPLIT) {
+      piece = bid % NP;
+      bid /= NP;
+    }
     const int rk = bid % p.num_seqs;
     g = bid / p.num_seqs;
     int b, r0, n, L;
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
       if (rk >= n_active) {
         // the rest of this head's ids are inactive requests too: go on at
         // the round that reaches the next head's first id
-        const int next = (g + 1) * qblocks * p.num_seqs - start;
+        const int next = (g + 1) * qblocks * NP * p.num_seqs - start;
         if (next >= nx) break;
         item = max(item, next / wx - 1);
         continue;
@@ -236,14 +242,17 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
     const int i0 = qb * TOK;
     if (i0 >= n || (n == 1 && p.skip_single)) continue;  // uniform
     const int prefix = L - n;
-    k_begin = 0;
-    k_end = prefix + min(i0 + TOK, n);  // keys this block can see
+    const int kend_blk = prefix + min(i0 + TOK, n);  // keys this block can see
+    // piece `piece` of the block's keys (the whole range when not split)
+    k_begin = SPLIT ? piece * p.piece_keys : 0;
+    if (SPLIT && k_begin >= kend_blk) continue;  // uniform: the block sees no key of this piece
+    k_end = SPLIT ? min(k_begin + p.piece_keys, kend_blk) : kend_blk;
     const int ti = i0 + (row % TOK);
     qvalid = head_ok && ti < n;
     q_row = r0 + ti;
     vis_lim = prefix + (qvalid ? ti : (n - 1));  // padding rows mask like the last token
     min_vis = prefix + i0;
-    has_keys = true;
+    has_keys = true;  // split: decided at the end (rows that see none of the piece write nothing)
     pt = p.page_table + (int64_t)b * p.pt_stride;
   } else {
     // work-group: key piece sp of row block rb of (group j, KV head g)
@@ -590,7 +599,24 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   // ---- normalise and write this lane's row
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
   if constexpr (!PREFIX) {
-    if (qvalid) {
+    if constexpr (SPLIT) {
+      // split keys: the piece's normalised output and log2-sum-exp, merged
+      // by extend_combine_kernel
+      if (qvalid && vis_lim >= k_begin) {
+        const float inv = 1.f / l_tot;
+        const int64_t part_row = ((int64_t)q_row * p.num_q_heads + (int64_t)g * G + hq) * p.num_pieces + piece;
+        float* op = p.o_part + part_row * D;
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = i * 32 + 8 * q4 + 4 * half;
+            *(float4*)(op + d) = make_float4(o[i][4 * q4 + 0] * inv, o[i][4 * q4 + 1] * inv,
+                                             o[i][4 * q4 + 2] * inv, o[i][4 * q4 + 3] * inv);
+          }
+        if (half == 0) p.lse[part_row] = m_ref * sl2 + __log2f(l_tot);
+      }
+    } else if (qvalid) {
     const float inv = 1.f / l_tot;
     uint16_t* op = (uint16_t*)p.out + ((int64_t)q_row * p.num_q_heads + (int64_t)g * G + hq) * D;
 #pragma unroll
@@ -626,11 +652,76 @@ __global__ __launch_bounds__(Shape<PREFIX>::kThreads, 2) void mfma_attn_kernel(c
   }  // items
 }
 
-template <int D, int G, bool PREFIX>
+// Split extend: one wave per (request b, row i < max_q_len, query head)
+// merges the key pieces of that row (workspace row: query row r0 + i, head).  Row i of request b sees
+// p_b + i + 1 keys, so it has ceil((p_b + i + 1) / piece_keys) pieces, each
+// with at least one visible key (written by the extend kernel); their
+// log-sum-exps are read one per lane and the partial outputs in batches of
+// eight independent loads.
+template <int D>
+__global__ __launch_bounds__(256) void extend_combine_kernel(const ExtendArgs p) {
+  constexpr int EPL = D / 64;
+  constexpr int BATCH = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads;
+  if (R >= rows) return;
+  const int hq = (int)(R % p.num_q_heads);
+  const int64_t bi = R / p.num_q_heads;
+  const int i = (int)(bi % p.max_q_len);
+  const int b = (int)(bi / p.max_q_len);
+  const int r0 = p.q_indptr[b];
+  const int n = p.q_indptr[b + 1] - r0;
+  if (i >= n) return;
+  const int vis = p.seq_lens[b] - n + i + 1;  // keys row i sees
+  const int ns = min((vis + p.piece_keys - 1) / p.piece_keys, p.num_pieces);
+  const int64_t wrow = ((int64_t)(r0 + i) * p.num_q_heads + hq) * p.num_pieces;  // the row's pieces
+  const float* lse = p.lse + wrow;
+  const float* op = p.o_part + wrow * D + lane * EPL;
+
+  float M = -INFINITY;
+  for (int c = 0; c < ns; c += 64) M = fmaxf(M, lse[min(c + lane, ns - 1)]);
+  M = wave_max(M);
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  if (ns > 0 && M != -INFINITY) {
+    float wsum = 0.f;
+    for (int c = 0; c < ns; c += 64) {
+      const float l = lse[min(c + lane, ns - 1)];
+      const float w = (c + lane < ns && l != -INFINITY) ? fast_exp2(l - M) : 0.f;
+      wsum += w;
+      const int cnt = min(64, ns - c);
+      for (int j0 = 0; j0 < cnt; j0 += BATCH) {
+        float wk[BATCH], v[BATCH][EPL];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const int j = min(j0 + k, cnt - 1);  // clamped: a real piece, weight zero below
+          wk[k] = j0 + k < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
+                               : 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[k][e] = op[(int64_t)(c + j) * D + e];
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = wk[k] > 0.f ? fmaf(wk[k], v[k][e], o[e]) : o[e];
+      }
+    }
+    wsum = wave_sum(wsum);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] /= wsum;
+  }
+  uint16_t* out = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + hq) * D + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(o[e]);
+}
+
+template <int D, int G, bool PREFIX, bool SPLIT>
 hipError_t launch_g(const ExtendArgs& a, hipStream_t stream) {
   constexpr int TOK = Shape<PREFIX>::kRows / G;
   const int64_t blocks_per = (a.max_q_len + TOK - 1) / TOK;
-  int64_t blocks = blocks_per * a.num_kv_heads * a.num_seqs * (PREFIX ? a.num_pieces : 1);
+  int64_t blocks = blocks_per * a.num_kv_heads * a.num_seqs * a.num_pieces;
   if (blocks == 0) return hipSuccess;
   if (!PREFIX) {
     // Up to four chip-fulls of items, one work-group per item: the
@@ -647,22 +738,26 @@ hipError_t launch_g(const ExtendArgs& a, hipStream_t stream) {
     if (cap >= 8 && blocks > 4 * cap) blocks = cap;
   }
   if (PREFIX && a.plan.plan) ++blocks;  // the work-group that writes the decode work order
-  hipLaunchKernelGGL((mfma_attn_kernel<D, G, PREFIX>), dim3((unsigned)blocks), dim3(Shape<PREFIX>::kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((mfma_attn_kernel<D, G, PREFIX, SPLIT>), dim3((unsigned)blocks), dim3(Shape<PREFIX>::kThreads),
+                     0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (!SPLIT || e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.num_seqs * a.max_q_len * a.num_q_heads;
+  hipLaunchKernelGGL((extend_combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool PREFIX>
+template <int D, bool PREFIX, bool SPLIT>
 hipError_t launch_d(const ExtendArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_g<D, 1, PREFIX>(a, stream);
-    case 2: return launch_g<D, 2, PREFIX>(a, stream);
-    case 3: return launch_g<D, 3, PREFIX>(a, stream);
-    case 4: return launch_g<D, 4, PREFIX>(a, stream);
-    case 5: return launch_g<D, 5, PREFIX>(a, stream);
-    case 6: return launch_g<D, 6, PREFIX>(a, stream);
-    case 7: return launch_g<D, 7, PREFIX>(a, stream);
-    case 8: return launch_g<D, 8, PREFIX>(a, stream);
+    case 1: return launch_g<D, 1, PREFIX, SPLIT>(a, stream);
+    case 2: return launch_g<D, 2, PREFIX, SPLIT>(a, stream);
+    case 3: return launch_g<D, 3, PREFIX, SPLIT>(a, stream);
+    case 4: return launch_g<D, 4, PREFIX, SPLIT>(a, stream);
+    case 5: return launch_g<D, 5, PREFIX, SPLIT>(a, stream);
+    case 6: return launch_g<D, 6, PREFIX, SPLIT>(a, stream);
+    case 7: return launch_g<D, 7, PREFIX, SPLIT>(a, stream);
+    case 8: return launch_g<D, 8, PREFIX, SPLIT>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -670,14 +765,15 @@ hipError_t launch_d(const ExtendArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) return launch_d<128, false>(a, stream);
-  if (a.head_dim == 64) return launch_d<64, false>(a, stream);
+  const bool split = a.num_pieces > 1;
+  if (a.head_dim == 128) return split ? launch_d<128, false, true>(a, stream) : launch_d<128, false, false>(a, stream);
+  if (a.head_dim == 64) return split ? launch_d<64, false, true>(a, stream) : launch_d<64, false, false>(a, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefix(const ExtendArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) return launch_d<128, true>(a, stream);
-  if (a.head_dim == 64) return launch_d<64, true>(a, stream);
+  if (a.head_dim == 128) return launch_d<128, true, false>(a, stream);
+  if (a.head_dim == 64) return launch_d<64, true, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -119,8 +119,8 @@ struct ExtendArgs {
   const int32_t* page_table;   // extend: per request; prefix: per group
   const int32_t* seq_lens;     // extend: [B]; prefix: shared lengths per request [B]
   void* out;                   // extend: [T_q, Hq, D] bf16
-  float* o_part;               // prefix: decode workspace partials
-  float* lse;
+  float* o_part;               // prefix: decode workspace partials; split extend: [T_q, Hq, num_pieces, D]
+  float* lse;                  // log2-sum-exp of each partial
   int64_t pt_stride;
   int32_t num_seqs;            // extend: requests; prefix: groups
   int32_t num_q_heads;
@@ -129,8 +129,8 @@ struct ExtendArgs {
   int32_t log2_page;
   int32_t max_q_len;           // extend: longest chunk; prefix: largest group
   int32_t max_keys;            // prefix: bound on the shared lengths (larger ones are clamped)
-  int32_t piece_keys;          // prefix: keys per piece
-  int32_t num_pieces;          // prefix: pieces per group
+  int32_t piece_keys;          // prefix and split extend: keys per piece
+  int32_t num_pieces;          // prefix: pieces per group; extend: pieces per request (1: not split)
   int32_t ws_pieces;           // prefix: workspace row stride in pieces
   int32_t skip_single;         // extend: leave requests with one new row to the decode kernels
   float scale_log2;

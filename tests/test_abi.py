@@ -53,9 +53,10 @@ def decode(p, fn="pa_decode", q=FAKE, Hq=32, pt=FAKE, stride=64, sl=FAKE, B=4, L
                                   Lmax, 0.1, split, out, ws, ws_bytes, None)
 
 
-def extend(p, q=FAKE, Hq=32, qi=FAKE, pt=FAKE, stride=64, sl=FAKE, B=2, qmax=128, Lmax=1000, out=FAKE):
+def extend(p, q=FAKE, Hq=32, qi=FAKE, pt=FAKE, stride=64, sl=FAKE, B=2, qmax=128, Lmax=1000, out=FAKE, split=0,
+           ws=FAKE, ws_bytes=1 << 40):
     return pa.load().pa_extend(ctypes.byref(p) if p is not None else None, q, Hq, qi, pt, stride, sl, B,
-                               qmax, Lmax, 0.1, out, None)
+                               qmax, Lmax, 0.1, split, out, ws, ws_bytes, None)
 
 
 def gather(p, pt=FAKE, stride=64, sl=FAKE, off=FAKE, B=2, Lmax=100, ko=FAKE, vo=FAKE):
@@ -217,6 +218,35 @@ def test_extend_validation():
     assert extend(p, out=FAKE + 4) == SHAPE
     assert extend(p, B=0) == OK
     assert extend(p, qmax=0) == OK
+    # split keys: invalid piece lengths, and the workspace they need
+    assert extend(p, split=100) == SHAPE
+    assert extend(p, split=-64) == SHAPE
+    assert extend(p, split=256, ws=0) == WS
+    assert extend(p, split=256, ws_bytes=1000) == WS
+    assert extend(p, split=256, ws=FAKE + 16) == WS
+    # no split (pieces at least max_seq_len): the workspace may be absent; the
+    # call then fails only on the next check (a null q), not on the workspace
+    assert extend(p, split=2048, ws=0, ws_bytes=0, q=0) == NULL
+
+
+def test_extend_split_plan_and_workspace():
+    lib = pa.load()
+    a256 = lambda x: (x + 255) // 256 * 256
+    # the Qwen3-8B-shaped chunked-prefill batch (8 requests x 16 blocks x 8 heads
+    # = 1024 items) fills the chip: not split, no workspace
+    assert lib.pa_extend_workspace_bytes(8, 512, 32, 8, 128, 4608, 0) == 0
+    # one request, a 512-token chunk after 32k cached keys (128 items): split
+    # into 8 pieces of 4160 keys
+    NP = 8
+    rows = 1 * 512 * 32 * NP
+    assert lib.pa_extend_workspace_bytes(1, 512, 32, 8, 128, 33280, 0) == a256(rows * 128 * 4) + a256(rows * 4)
+    # short keys are never split automatically
+    assert lib.pa_extend_workspace_bytes(1, 512, 32, 8, 128, 900, 0) == 0
+    # explicit pieces
+    rows = 2 * 100 * 8 * 4
+    assert lib.pa_extend_workspace_bytes(2, 100, 8, 2, 64, 1000, 256) == a256(rows * 64 * 4) + a256(rows * 4)
+    assert lib.pa_extend_workspace_bytes(2, 100, 8, 2, 64, 1000, 1024) == 0  # one piece covers the keys
+    assert lib.pa_extend_workspace_bytes(2, 100, 8, 2, 64, 1000, 100) == 0   # invalid
 
 
 def cascade(p, q=FAKE, Hq=32, pt=FAKE, stride=64, sl=FAKE, B=32, Lmax=1000, gs=FAKE, ng=2, gmax=16,

@@ -188,6 +188,47 @@ def test_extend_sweep(case):
     assert_close(out, ref, f"extend sweep {case}")
 
 
+EXTEND_SPLIT = [
+    # (prefixes, chunks, Hq, Hkv, D, P, split): keys cut into pieces merged by
+    # the combine kernel; rows of the first pieces see every key of a piece,
+    # the last piece of a block is causal
+    ([0, 64, 1000], [128, 129, 33], 32, 8, 128, 16, 64),
+    ([3000, 17], [100, 300], 32, 8, 128, 16, 192),
+    ([300, 0, 77], [200, 64, 19], 14, 2, 64, 16, 128),        # group 7
+    ([5000, 0, 900], [40, 0, 1], 8, 2, 128, 1, 1024),        # an empty request, a one-row chunk, page size 1
+    ([20000], [300], 32, 8, 128, 16, 0),                      # automatic: one long-prefix request is split
+    ([4000, 6000], [64, 512], 40, 8, 128, 16, 0),             # automatic, group 5
+]
+
+
+@pytest.mark.parametrize("case", range(len(EXTEND_SPLIT)))
+def test_extend_split_keys(case):
+    prefixes, chunks, Hq, Hkv, D, P, split = EXTEND_SPLIT[case]
+    lens = [p + n for p, n in zip(prefixes, chunks)]
+    wl = W.make_custom(lens, Hq, Hkv, D, P, dtype="bf16", kind="extend", n_new=chunks, seed=260 + case)
+    nbytes = pa().extend_workspace_bytes(wl.num_seqs, wl.max_q_len, Hq, Hkv, D, wl.max_seq_len, split)
+    banner(f"extend split {case}: prefixes={prefixes} chunks={chunks} Hq={Hq} Hkv={Hkv} D={D} P={P} "
+           f"split={split} workspace={nbytes}")
+    assert nbytes > 0, "this case is meant to split the keys"
+    dw = fresh(wl)
+    T = torch()
+    o1 = pa().extend(dw.q, dw.q_indptr, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_q_len,
+                     wl.max_seq_len, wl.scale, split_tokens=split)
+    o2 = pa().extend(dw.q, dw.q_indptr, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_q_len,
+                     wl.max_seq_len, wl.scale, split_tokens=split)
+    T.cuda.synchronize()
+    assert T.equal(o1.view(T.int16), o2.view(T.int16)), "split extend is not deterministic"
+    kp, vp = stored_oracle_pools(wl)
+    ref = oracle.extend(wl.q, wl.q_indptr, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    err = assert_close(f64(o1), ref, f"extend split {case}")
+    # the unsplit kernel on the same inputs
+    whole = pa().extend(dw.q, dw.q_indptr, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_q_len,
+                        wl.max_seq_len, wl.scale, split_tokens=(wl.max_seq_len + 63) // 64 * 64)
+    T.cuda.synchronize()
+    assert_close(f64(o1), f64(whole), f"extend split {case} vs unsplit")
+    print(f"[result] extend split {case}: max abs err {err:.3g}", flush=True)
+
+
 def test_empty_batch_is_a_no_op():
     banner("empty batch")
     T = torch()

@@ -4,10 +4,11 @@
 One step = one decode layer-step of the Qwen3-8B-shaped batch with radix
 prefix sharing (256 requests, log-uniform lengths 512..8192, 32 query / 8 KV
 heads, head_dim 128, page 16, bf16; groups of 16 requests share a 1024-token
-prefix): kv_store of the 256 new K/V rows, then the cascade decode (shared
+prefix): the store of the 256 new K/V rows, then the cascade decode (shared
 prefix pass on the matrix cores, each request's own keys through the split-K
-decode kernel, combine), the shared-prefix pass on a second stream beside the
-store, the work order and the own-keys pass.  The same calls one after the other on one stream give the
+decode kernel, combine).  The store and the own-keys pass's work order are
+one launch; the shared-prefix pass runs on a second stream beside it and the
+own-keys pass.  The same calls one after the other on one stream give the
 per-kernel times.  Inputs are resident in HBM before timing starts.
 The plain decode (partial + combine over every request's whole page list) and
 the chunked-prefill extend call (8 requests, prefix 0..4096 + 512-token
@@ -84,10 +85,10 @@ def sources_digest(paths):
     return h.hexdigest()[:16]
 
 
-def read_traffic(path):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, if it was taken on the current kernel source."""
-    fname = PROFILE_COUNTERS[path]
+def read_profile(kind):
+    """The fields of a committed counter summary, if it was taken on the
+    current kernel source (its source_digest matches), else None."""
+    fname = PROFILE_COUNTERS[kind]
     if not os.path.exists(fname):
         return None
     kv = {}
@@ -95,15 +96,52 @@ def read_traffic(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != sources_digest(KERNEL_SOURCES[path]):
+    if kv.get("source_digest") != sources_digest(KERNEL_SOURCES[kind]):
         return None
+    return kv
+
+
+def read_traffic(kind):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    kv = read_profile(kind)
     try:
-        return float(kv["hbm_bytes_per_dispatch"])
+        return float(kv["hbm_bytes_per_dispatch"]) if kv else None
     except (KeyError, ValueError):
         return None
 
 
+def read_mfma_counters():
+    """Matrix-core use of the extend kernel from its committed counter
+    summary (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of the launch,
+    the clock under load from GRBM_GUI_ACTIVE), if taken on the current
+    source."""
+    kv = read_profile("extend")
+    keys = ("mfma_busy_frac", "clock_ghz_under_load", "peak_tflops_at_that_clock", "mfma_flops_executed",
+            "valu_coexec_frac_of_mfma_busy", "lds_bank_conflict_cycles", "valu_insts_per_mfma")
+    if not kv or any(k not in kv for k in keys):
+        return None
+    return {k: float(kv[k]) for k in keys}
+
+
 COPY_PAGES = 16384  # per pool: 16384 pages x 16 tokens x 8 heads x 128 x bf16 = 512 MiB
+
+
+def read_ceiling(iters=10, nbytes=2 << 30):
+    """Read-only HBM rate through the library's calibration call
+    (pa_stream_read over a 2 GiB buffer, far larger than the last-level
+    cache): the ceiling the streaming kernels are compared with."""
+    import torch
+
+    import paged_kv_attention_11_amd as pa
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = _time(torch, stream, lambda: pa.stream_read(buf, sink), iters)
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def copy_calibration(iters=10):
@@ -380,6 +418,8 @@ def bench_extend(pa, W, torch, np, stream, iters, warmup=3):
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": read_traffic("extend"), "algorithmic_flops_per_launch": flops},
+        # rocprofv3 counters of the same kernel on the same workload (committed summary)
+        "mfma_counters": read_mfma_counters(),
     }
 
 
@@ -426,6 +466,39 @@ def cpu_baseline(wl, target_s):
         "host_cpus": os.cpu_count(),
         "requests_per_s": round(done / t_used, 2),
     }
+
+
+class StreamSync:
+    """Orders one stream after another's enqueued work with HIP events that
+    carry no system-scope fence (hipEventDisableSystemFence): both streams
+    are on this device, so the device-scope ordering of the event suffices,
+    and each cross-stream hop costs less.  Plumbing around torch's streams,
+    through the HIP runtime (the library itself does not touch events)."""
+
+    def __init__(self, slots=2):
+        import ctypes
+
+        self._c = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        flags = 0x2 | 0x20000000  # hipEventDisableTiming | hipEventDisableSystemFence
+        self._ev = []
+        for _ in range(slots):
+            e = ctypes.c_void_p()
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(e), flags) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self._ev.append(e)
+
+    def order(self, stream, after, slot):
+        """Work enqueued on `stream` from now on starts after the work already
+        enqueued on `after`."""
+        e = self._ev[slot]
+        if self._hip.hipEventRecord(e, self._c.c_void_p(after.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        if self._hip.hipStreamWaitEvent(self._c.c_void_p(stream.cuda_stream), e, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
 
 
 def main():
@@ -517,25 +590,28 @@ def main():
         new_pages = set((wl.slot_mapping[wl.slot_mapping >= 0] // P).tolist())
         assert not (shared_pages & new_pages), "a new row lands on a shared prefix page"
 
+    sync = StreamSync()
+
     def step_overlapped():
         """The timed step.  Cascade: the shared-prefix pass (one latency-bound
         work-group per compute unit) on a second stream from the start of the
         step, beside the store, the work order and the HBM-bound own-keys
         pass; the merge after both.  The prefix pass reads only keys below
         each request's shared length, on the groups' prefix pages, which this
-        step's store does not write (checked below), so it does not wait for
+        step's store does not write (checked above), so it does not wait for
         the store, and its work-groups take their compute units before the
-        own-keys pass fills the rest."""
+        own-keys pass fills the rest.  The two streams are ordered by events
+        without a system-scope fence (both sides are on this device)."""
         if not cascade:
             return step()
         cur = torch.cuda.current_stream()
-        side.wait_stream(cur)
+        sync.order(side, after=cur, slot=0)
         with torch.cuda.stream(side):
             call("prefix")
         pa.kv_store(dw.k_pool, dw.v_pool, dw.k_new, dw.v_new, dw.slot_mapping)
         call("order")
         call("suffix")
-        cur.wait_stream(side)
+        sync.order(cur, after=side, slot=1)
         call("combine")
 
     for _ in range(args.warmup):
@@ -570,6 +646,16 @@ def main():
     ms_step = total_ms / args.steps
     log(f"decode ({args.path}): {ms_step * 1e3:.1f} us/step ({ms_sequential * 1e3:.1f} us one call after the "
         f"other: " + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in stage_ms.items()) + f") (wall {wall:.3f}s)")
+
+    # The timed (two-stream) step must give the same bits as the calls one
+    # after the other on one stream.
+    overlapped_out = out.clone()
+    out.zero_()
+    step()
+    torch.cuda.synchronize()
+    overlapped_same = bool(torch.equal(out.view(torch.int16), overlapped_out.view(torch.int16)))
+    if not overlapped_same:
+        log("WARNING: the timed two-stream step differs from the sequential step")
 
     # The same step captured once into a HIP graph and replayed (how a serving
     # loop would launch it): the launch gaps between its kernels shrink.  The
@@ -636,9 +722,9 @@ def main():
             "description": W.DESCRIPTIONS.get(args.config, args.config),
             "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
             "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "split_tokens": split,
-            "step": "kv_store + " + ("decode_cascade stages (prefix pass on a second stream beside the store, "
-                                     "the work order and the own-keys pass, then combine)" if cascade
-                                     else "decode_partial + decode_combine"),
+            "step": ("decode_cascade stages: the store of the 256 new rows and the work order in one launch, "
+                     "the own-keys pass, the prefix pass on a second stream beside them, then combine" if cascade
+                     else "kv_store + decode_partial + decode_combine"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
@@ -651,6 +737,7 @@ def main():
                          "GBps_unique": round(kv_unique / (ms_graph * 1e-3) / 1e9, 2),
                          "pct_of_hbm_peak": round(100 * kv_unique / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                          "same_bits_as_eager": graph_same},
+        "timed_step_same_bits_as_sequential": overlapped_same,
         "roofline": {
             "kernel": dom_kernel,
             "bound": "hbm",
@@ -730,10 +817,15 @@ def main():
         log(f"mixed step: eager {m['eager_us']} us, graph {m['graph_replay_us']} us, "
             f"all-extend attention {m['attention_all_extend_us']} us vs routed {m['attention_routed_us']} us")
 
-    # ---------------- plain-copy reference on the same device
+    # ---------------- plain-copy reference and read-only ceiling on the same device
     cgb, _, _ = copy_calibration()
     result["copy_reference_GBps"] = round(cgb, 1)
-    log(f"plain copy: {cgb:.0f} GB/s read+write")
+    rgb = read_ceiling()
+    result["hbm_read_ceiling_GBps"] = round(rgb, 1)
+    result["roofline"]["frac_of_read_ceiling"] = round(result["roofline"]["achieved"] / rgb, 4)
+    result["value_frac_of_read_ceiling"] = round(result["value"] / rgb, 4)
+    log(f"plain copy: {cgb:.0f} GB/s read+write; read-only ceiling {rgb:.0f} GB/s "
+        f"(dominant kernel at {100 * result['roofline']['achieved'] / rgb:.1f}% of it)")
 
     # ---------------- CPU oracle on a bounded sample (rank 0, N=1 only)
     if not args.no_cpu_baseline:

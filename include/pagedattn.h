@@ -341,6 +341,15 @@ pa_status pa_extend(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
  *                       (pa_cascade_piece_keys), else a positive multiple of
  *                       64.
  *   split_tokens        as for pa_decode.
+ *   k_new, v_new, slot_mapping, num_new_rows
+ *                       optional (NULL, NULL, NULL, 0): the step's new K/V
+ *                       rows, stored exactly as pa_kv_store would store them
+ *                       (same layout, alignment and slot contract), by the
+ *                       same launch that writes the work order of kernel 2
+ *                       (one launch fewer in the step).  They are stored
+ *                       before kernel 2 reads any key; the new rows must not
+ *                       land on pages holding shared keys (a radix cache
+ *                       writes a new token to a page of its own request).
  *   workspace           >= pa_decode_cascade_workspace_bytes(...) bytes,
  *                       256-byte aligned, clobbered.  Layout: fp32 partial
  *                       outputs [num_seqs, num_q_heads, NP + S, head_dim],
@@ -364,14 +373,17 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
                             int32_t num_seqs, int32_t max_seq_len, const int32_t* group_starts,
                             int32_t num_groups, int32_t max_group_size, const int32_t* prefix_page_table,
                             int32_t prefix_pt_stride, const int32_t* shared_lens, int32_t max_shared_len,
-                            float scale, int32_t split_tokens, int32_t prefix_piece_keys, void* out,
+                            float scale, int32_t split_tokens, int32_t prefix_piece_keys, const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_new_rows, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The stages of pa_decode_cascade, one kernel each, callable one at a time on
  * one workspace (same arguments; each validates them all):
  *   _order    the work order of kernel 2 (a one-work-group kernel; nothing
- *             when kernel 2 runs without one, i.e. on small batches);
+ *             when kernel 2 runs without one, i.e. on small batches), and
+ *             the store of the new rows when they are given (in the same
+ *             launch); the other stages ignore the new rows;
  *   _prefix   kernel 1 alone (nothing when there is no shared prefix);
  *   _suffix   kernel 2: reads the work order _order wrote;
  *   _combine  kernel 3: after both _prefix and _suffix.
@@ -381,9 +393,10 @@ pa_status pa_decode_cascade(const pa_kv_pool* pool, const void* q, int32_t num_q
  * _suffix reads the step's new rows, so it follows their store; _prefix reads
  * only the keys below each request's shared length, so it may even run
  * beside the store when no new row lands on those prefix pages (a radix
- * cache writes a new token to a page of its own request).  Called as pa_decode_cascade,
- * the work order is written by one extra work-group of kernel 1 instead (one
- * launch fewer).  A work order written for another batch gives wrong rows but
+ * cache writes a new token to a page of its own request).  Called as
+ * pa_decode_cascade without new rows, the work order is written by one extra
+ * work-group of kernel 1 instead (one launch fewer); with new rows, the
+ * order-and-store launch comes first.  A work order written for another batch gives wrong rows but
  * no access outside the requests' pages.
  */
 pa_status pa_decode_cascade_prefix(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
@@ -392,7 +405,8 @@ pa_status pa_decode_cascade_prefix(const pa_kv_pool* pool, const void* q, int32_
                                    int32_t num_groups, int32_t max_group_size,
                                    const int32_t* prefix_page_table, int32_t prefix_pt_stride,
                                    const int32_t* shared_lens, int32_t max_shared_len, float scale,
-                                   int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                   int32_t split_tokens, int32_t prefix_piece_keys, const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_new_rows, void* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 pa_status pa_decode_cascade_suffix(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                                    const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
@@ -400,7 +414,8 @@ pa_status pa_decode_cascade_suffix(const pa_kv_pool* pool, const void* q, int32_
                                    int32_t num_groups, int32_t max_group_size,
                                    const int32_t* prefix_page_table, int32_t prefix_pt_stride,
                                    const int32_t* shared_lens, int32_t max_shared_len, float scale,
-                                   int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                   int32_t split_tokens, int32_t prefix_piece_keys, const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_new_rows, void* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                                     const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
@@ -408,7 +423,8 @@ pa_status pa_decode_cascade_combine(const pa_kv_pool* pool, const void* q, int32
                                     int32_t num_groups, int32_t max_group_size,
                                     const int32_t* prefix_page_table, int32_t prefix_pt_stride,
                                     const int32_t* shared_lens, int32_t max_shared_len, float scale,
-                                    int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                    int32_t split_tokens, int32_t prefix_piece_keys, const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_new_rows, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 pa_status pa_decode_cascade_order(const pa_kv_pool* pool, const void* q, int32_t num_q_heads,
                                   const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
@@ -416,7 +432,8 @@ pa_status pa_decode_cascade_order(const pa_kv_pool* pool, const void* q, int32_t
                                   int32_t num_groups, int32_t max_group_size,
                                   const int32_t* prefix_page_table, int32_t prefix_pt_stride,
                                   const int32_t* shared_lens, int32_t max_shared_len, float scale,
-                                  int32_t split_tokens, int32_t prefix_piece_keys, void* out, void* workspace,
+                                  int32_t split_tokens, int32_t prefix_piece_keys, const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_new_rows, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
 /*
@@ -536,6 +553,16 @@ pa_status pa_check_cascade(const pa_kv_pool* pool, const int32_t* page_table, in
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,
                     const int32_t* seq_lens, const int64_t* out_offsets, int32_t num_seqs,
                     int32_t max_seq_len, void* k_out, void* v_out, void* stream);
+
+/*
+ * pa_stream_read: read `bytes` (a multiple of 16) of device memory at src
+ * (16-byte aligned) with plain 16-byte vector loads and OR a nonzero digest
+ * of them into *sink (a uint32 in device memory; the value has no meaning
+ * beyond keeping the loads live).  Calibration helper: the read-only HBM
+ * rate this device reaches, the ceiling the streaming kernels (decode,
+ * verify) are measured against beside the 8 TB/s peak.
+ */
+pa_status pa_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -59,7 +59,7 @@ _POOLP = ctypes.POINTER(KVPool)
 _DECODE_ARGS = [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]
 
 _CASCADE_ARGS = [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
-                 _i32, _vp, _vp, _sz, _vp]
+                 _i32, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]
 
 SIGNATURES = {
     # name: (restype, argtypes) -- mirrors include/pagedattn.h
@@ -90,6 +90,7 @@ SIGNATURES = {
     "pa_check_batch": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i64, _vp, _vp]),
     "pa_check_cascade": (_i32, [_POOLP, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp]),
     "pa_gather": (_i32, [_POOLP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "pa_stream_read": (_i32, [_vp, _i64, _vp, _vp]),
 }
 
 
@@ -360,16 +361,27 @@ def decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim
 
 def decode_cascade(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, group_starts, max_group_size,
                    prefix_page_table, shared_lens, max_shared_len, scale, out=None, workspace=None,
-                   split_tokens=0, prefix_piece_keys=0, stream=None, stage=None):
+                   split_tokens=0, prefix_piece_keys=0, stream=None, stage=None, k_new=None, v_new=None,
+                   slot_mapping=None):
     """Decode of requests that share prefix pages: group j is requests
     group_starts[j]..group_starts[j+1]-1, whose first shared_lens[b] keys sit
     on prefix_page_table[j].  Same result as decode(...).  `stage` ("order",
     "prefix", "suffix" or "combine") enqueues only that kernel ("order" before
     "suffix"; "prefix" may run on another stream beside those two; "combine"
-    after all three)."""
+    after all three).  k_new, v_new [N, H_kv, D] and slot_mapping int64 [N]
+    (optional): the step's new rows, stored by the work-order launch (the
+    single call, or stage "order") as kv_store(...) would."""
     torch = _torch()
     pool = make_pool(k_pool, v_pool)
     _dev(q, "q", torch.bfloat16)
+    n_new = 0
+    if slot_mapping is not None:
+        _dev(k_new, "k_new", k_pool.dtype)
+        _dev(v_new, "v_new", k_pool.dtype)
+        _dev(slot_mapping, "slot_mapping", torch.int64)
+        n_new = slot_mapping.numel()
+        if k_new.shape[0] != n_new or v_new.shape[0] != n_new:
+            raise ValueError("k_new, v_new and slot_mapping must have the same number of rows")
     for t, n in ((page_table, "page_table"), (seq_lens, "seq_lens"), (group_starts, "group_starts"),
                  (prefix_page_table, "prefix_page_table"), (shared_lens, "shared_lens")):
         _dev(t, n, torch.int32)
@@ -396,8 +408,9 @@ def decode_cascade(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, group_s
         ctypes.byref(pool), _ptr(q), q.shape[1], _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,
         int(max_seq_len), _ptr(group_starts), ng, int(max_group_size), _ptr(prefix_page_table),
         prefix_page_table.shape[1], _ptr(shared_lens), int(max_shared_len), float(scale), int(split_tokens),
-        int(prefix_piece_keys), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream))
+        int(prefix_piece_keys), _ptr(k_new if n_new else None), _ptr(v_new if n_new else None),
+        _ptr(slot_mapping if n_new else None), n_new, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, fn)
     return out
 
@@ -535,3 +548,12 @@ def gather(k_pool, v_pool, page_table, seq_lens, out_offsets, max_seq_len, k_out
                           _ptr(out_offsets), seq_lens.numel(), int(max_seq_len), _ptr(k_out), _ptr(v_out),
                           _stream(stream))
     _check(st, "pa_gather")
+
+
+def stream_read(src, sink, stream=None):
+    """Read every byte of the GPU tensor `src` (calibration of the read-only
+    HBM rate); ORs a nonzero digest into `sink` (int32 [1] on the GPU)."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    st = load().pa_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream))
+    _check(st, "pa_stream_read")

@@ -573,10 +573,11 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
 namespace {
 
 // Stages: the shared-prefix pass, the own-keys pass, the merge, and the own-keys
-// pass's work order.  Called together (pa_decode_cascade), the work order is
-// written by one extra work-group of the shared-prefix pass; called one at a
-// time, each stage is one kernel, so the shared-prefix pass may run on
-// another stream beside the work order and the own-keys pass.
+// pass's work order (with the store of the step's new rows when they are
+// given).  Called together (pa_decode_cascade) without new rows, the work
+// order is written by one extra work-group of the shared-prefix pass; called
+// one at a time, each stage is one kernel, so the shared-prefix pass may run
+// on another stream beside the work order and the own-keys pass.
 enum : unsigned { kStagePrefix = 1, kStageSuffix = 2, kStageCombine = 4, kStageOrder = 8, kStageAll = 15 };
 
 // The cascade decode's validation, plan and the enqueueing of the selected
@@ -586,13 +587,18 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
                        const int32_t* group_starts, int32_t num_groups, int32_t max_group_size,
                        const int32_t* prefix_page_table, int32_t prefix_pt_stride, const int32_t* shared_lens,
                        int32_t max_shared_len, float scale, int32_t split_tokens, int32_t prefix_piece_keys,
+                       const void* k_new, const void* v_new, const int64_t* slot_mapping, int64_t num_new_rows,
                        void* out, void* workspace, size_t workspace_bytes_, void* stream, unsigned stages) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (pool->dtype != PA_BF16) return PA_ERR_DTYPE;
   if (num_seqs < 0 || max_seq_len < 0 || pt_stride < 0 || num_q_heads <= 0 || num_groups < 0 ||
-      max_group_size < 0 || prefix_pt_stride < 0 || max_shared_len < 0)
+      max_group_size < 0 || prefix_pt_stride < 0 || max_shared_len < 0 || num_new_rows < 0)
     return PA_ERR_SHAPE;
+  if (num_new_rows > 0) {  // the step's new rows, stored by the work-order stage
+    if (!k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return PA_ERR_SHAPE;
+  }
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int G = num_q_heads / pool->num_kv_heads;
   if (G < 1 || G > kMaxGroup) return PA_ERR_UNSUPPORTED;
@@ -653,9 +659,29 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   a.plan = use_plan(num_seqs, pool->num_kv_heads, S)
                ? (int4*)((char*)lse + align256(rows * sizeof(float)))
                : nullptr;
+  // The work order of pass 2 (when it has one) and the store of the step's
+  // new rows (when given) in one launch.  Called together without new rows,
+  // one extra work-group of pass 1 writes the order instead.
+  const bool store_rows = num_new_rows > 0;
+  const bool order_in_prefix = !store_rows && prefix_pass && (stages & kStagePrefix) && (stages & kStageOrder);
+  if ((stages & kStageOrder) && !order_in_prefix) {  // no-op without an order or rows
+    if (store_rows) {
+      pa::StoreArgs sa;
+      sa.k_new = k_new;
+      sa.v_new = v_new;
+      sa.slot_mapping = slot_mapping;
+      sa.k_pool = pool->k_pool;
+      sa.v_pool = pool->v_pool;
+      sa.num_rows = num_new_rows;
+      sa.row_chunks = pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype) / 16;
+      st = hip_status(pa::launch_decode_plan_store(plan_args(a), sa, hs));
+    } else {
+      st = hip_status(pa::launch_decode_plan(plan_args(a), hs));
+    }
+    if (st != PA_OK) return st;
+  }
   // pass 1: each group's shared pages, all members' queries in one tile, and
-  // (all stages in one call) the work order of pass 2 when it has one
-  const bool order_in_prefix = prefix_pass && (stages & kStagePrefix) && (stages & kStageOrder);
+  // (all stages in one call, no new rows) the work order of pass 2
   if (prefix_pass && (stages & kStagePrefix)) {
     pa::ExtendArgs e = {};
     e.k_pool = pool->k_pool;
@@ -683,10 +709,6 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
     st = hip_status(pa::launch_prefix(e, hs));
     if (st != PA_OK) return st;
   }
-  if ((stages & kStageOrder) && !order_in_prefix) {  // no-op when pass 2 has no work order
-    st = hip_status(pa::launch_decode_plan(plan_args(a), hs));
-    if (st != PA_OK) return st;
-  }
 
   if (stages & kStageSuffix) {
     st = hip_status(pa::launch_decode_partial(a, hs));
@@ -705,11 +727,12 @@ extern "C" {
       const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, const int32_t *group_starts,          \
       int32_t num_groups, int32_t max_group_size, const int32_t *prefix_page_table, int32_t prefix_pt_stride, \
       const int32_t *shared_lens, int32_t max_shared_len, float scale, int32_t split_tokens,                 \
-      int32_t prefix_piece_keys, void *out, void *workspace, size_t workspace_bytes_, void *stream
+      int32_t prefix_piece_keys, const void *k_new, const void *v_new, const int64_t *slot_mapping,          \
+      int64_t num_new_rows, void *out, void *workspace, size_t workspace_bytes_, void *stream
 #define PA_CASCADE_ARGS                                                                                    \
   pool, q, num_q_heads, page_table, pt_stride, seq_lens, num_seqs, max_seq_len, group_starts, num_groups, \
       max_group_size, prefix_page_table, prefix_pt_stride, shared_lens, max_shared_len, scale, split_tokens, \
-      prefix_piece_keys, out, workspace, workspace_bytes_, stream
+      prefix_piece_keys, k_new, v_new, slot_mapping, num_new_rows, out, workspace, workspace_bytes_, stream
 
 pa_status pa_decode_cascade(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStageAll); }
 pa_status pa_decode_cascade_prefix(PA_CASCADE_PARAMS) { return cascade_impl(PA_CASCADE_ARGS, kStagePrefix); }
@@ -886,6 +909,14 @@ pa_status pa_check_cascade(const pa_kv_pool* pool, const int32_t* page_table, in
   a.max_shared_len = max_shared_len;
   a.page_size = pool->page_size;
   return hip_status(pa::launch_check_cascade(a, (hipStream_t)stream));
+}
+
+pa_status pa_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0) return PA_ERR_SHAPE;
+  if (bytes == 0) return PA_OK;
+  if (!src || !sink) return PA_ERR_NULL;
+  if (!aligned(src, 16) || bytes % 16 != 0 || !aligned(sink, 4)) return PA_ERR_SHAPE;
+  return hip_status(pa::launch_stream_read(src, bytes, sink, (hipStream_t)stream));
 }
 
 pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t pt_stride,

@@ -150,6 +150,39 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const PlanArg
   build_decode_plan<kPlanThreads>(p);
 }
 
+// The work order and the store of the step's new rows in one launch (they
+// are independent): work-group 0 writes the order when there is one, the
+// other work-groups copy new row i to flat slot slot_mapping[i] of both pools
+// (negative slots are padding), one 16-byte piece per lane, as
+// kv_store_kernel does.  One launch instead of two takes a kernel and a
+// launch gap off the critical path of a decode step.
+template <int kPlanThreads>
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_store_kernel(const PlanArgs p, const StoreArgs s) {
+  int first = 0;
+  if (p.plan) {
+    if (blockIdx.x == 0) {
+      build_decode_plan<kPlanThreads>(p);
+      return;
+    }
+    first = 1;
+  }
+  const uint4* k_new = (const uint4*)s.k_new;
+  const uint4* v_new = (const uint4*)s.v_new;
+  uint4* k_pool = (uint4*)s.k_pool;
+  uint4* v_pool = (uint4*)s.v_pool;
+  const int64_t total = s.num_rows * s.row_chunks;
+  const int64_t stride = (int64_t)(gridDim.x - first) * kPlanThreads;
+  for (int64_t i = (int64_t)(blockIdx.x - first) * kPlanThreads + threadIdx.x; i < total; i += stride) {
+    const int64_t row = i / s.row_chunks;
+    const int64_t c = i - row * s.row_chunks;
+    const int64_t slot = s.slot_mapping[row];
+    if (slot < 0) continue;
+    const int64_t dst = slot * s.row_chunks + c;
+    k_pool[dst] = k_new[i];
+    v_pool[dst] = v_new[i];
+  }
+}
+
 // NT: the keys are read once per step and nowhere else (each request's own
 // keys in the cascade), so they are loaded nontemporally and leave the
 // caches to the data that is read again (the groups' shared pages, the
@@ -649,6 +682,23 @@ hipError_t launch_decode_plan(const PlanArgs& p, hipStream_t stream) {
     hipLaunchKernelGGL(decode_plan_kernel<256>, dim3(1), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_plan_kernel<1024>, dim3(1), dim3(1024), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_plan_store(const PlanArgs& p, const StoreArgs& s, hipStream_t stream) {
+  const bool plan = p.plan && p.num_seqs > 0 && p.max_splits > 0;
+  const int64_t total = s.num_rows * s.row_chunks;
+  if (!plan && total == 0) return hipSuccess;
+  PlanArgs pp = p;
+  if (!plan) pp.plan = nullptr;
+  const int threads = plan && p.num_seqs > 256 ? 1024 : 256;
+  int64_t store_blocks = (total + threads - 1) / threads;
+  if (store_blocks > 8192) store_blocks = 8192;
+  const dim3 grid((unsigned)(store_blocks + (plan ? 1 : 0)));
+  if (threads == 256)
+    hipLaunchKernelGGL(decode_plan_store_kernel<256>, grid, dim3(256), 0, stream, pp, s);
+  else
+    hipLaunchKernelGGL(decode_plan_store_kernel<1024>, grid, dim3(1024), 0, stream, pp, s);
   return hipGetLastError();
 }
 

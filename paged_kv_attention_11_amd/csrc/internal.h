@@ -197,10 +197,14 @@ struct CascadeCheckArgs {
 
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_rope_store(const RopeArgs& a, hipStream_t stream);
 // Return hipErrorInvalidValue for an instantiation that does not exist
 // (the ABI layer validates first, so this is a guard, not a code path).
 hipError_t launch_decode_plan(const PlanArgs& p, hipStream_t stream);
+// The work order (when p.plan is set) and the store of s.num_rows new rows in
+// one launch.
+hipError_t launch_decode_plan_store(const PlanArgs& p, const StoreArgs& s, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);

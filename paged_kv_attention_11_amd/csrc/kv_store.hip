@@ -71,7 +71,70 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint4* __restric
   }
 }
 
+// Read-only streaming calibration.  The buffer is cut into chunks of
+// kReadChunk 16-byte pieces (32 KB) and every work-group reads its own run of
+// consecutive chunks, one chunk per iteration: wave w of the work-group reads
+// the 8 KB of the chunk from byte 8 KB w, lane l the 16 bytes at 1 KB u +
+// 16 l of it for u < kReadUnroll, all loads issued before any is used.  The
+// XOR of what it read is folded over the work-group and one lane ORs it into
+// the sink, so no load is dead.  Measures the HBM read rate the device
+// reaches with plain vector loads, the ceiling the streaming kernels are
+// compared with.
+constexpr int kReadUnroll = 8;
+constexpr int64_t kReadChunk = (int64_t)kThreads * kReadUnroll;
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  __shared__ uint32_t s_x[kThreads / 64];
+  uint32_t x = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nfull = n16 / kReadChunk;  // whole chunks
+  const int64_t per = (nfull + gridDim.x - 1) / gridDim.x;  // chunks per work-group
+  const int64_t c0 = (int64_t)blockIdx.x * per;
+  const int64_t c1 = c0 + per < nfull ? c0 + per : nfull;
+  for (int64_t c = c0; c < c1; ++c) {
+    const uint4* p = src + c * kReadChunk + wave * (kReadUnroll * 64) + lane;
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = p[u * 64];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  // the pieces after the last whole chunk
+  for (int64_t i = nfull * kReadChunk + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads) {
+    const uint4 v = src[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x ^= (uint32_t)__shfl_xor((int)x, m, 64);
+  if (lane == 0) s_x[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kThreads / 64; ++w) t ^= s_x[w];
+    atomicOr(sink, t | 1u);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // eight 256-thread work-groups per compute unit: enough loads in flight
+  int64_t blocks = (int64_t)cus * 8;
+  const int64_t need = (n16 + kThreads - 1) / kThreads;
+  if (blocks > need) blocks = need;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, (const uint4*)src, n16,
+                     sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t total = a.num_rows * a.row_chunks;

@@ -251,9 +251,9 @@ def test_extend_split_plan_and_workspace():
 
 def cascade(p, q=FAKE, Hq=32, pt=FAKE, stride=64, sl=FAKE, B=32, Lmax=1000, gs=FAKE, ng=2, gmax=16,
             ppt=FAKE, pstride=8, shl=FAKE, msh=128, split=0, pk=0, out=FAKE, ws=FAKE, ws_bytes=1 << 40,
-            fn="pa_decode_cascade"):
+            fn="pa_decode_cascade", kn=0, vn=0, sm=0, nn=0):
     return getattr(pa.load(), fn)(ctypes.byref(p), q, Hq, pt, stride, sl, B, Lmax, gs, ng, gmax, ppt,
-                                  pstride, shl, msh, 0.1, split, pk, out, ws, ws_bytes, None)
+                                  pstride, shl, msh, 0.1, split, pk, kn, vn, sm, nn, out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("fn", ["pa_decode_cascade", "pa_decode_cascade_prefix", "pa_decode_cascade_suffix", "pa_decode_cascade_order",
@@ -281,6 +281,12 @@ def test_cascade_validation(fn):
     assert cascade(p, ws_bytes=4096) == WS
     assert cascade(p, q=FAKE + 2) == SHAPE
     assert cascade(p, B=0, gmax=0, ng=0, q=0, pt=0, sl=0, out=0, ws=0) == OK  # empty batch
+    # the step's new rows (stored by the work-order launch)
+    assert cascade(p, nn=-1) == SHAPE
+    assert cascade(p, nn=4, kn=0, vn=FAKE, sm=FAKE) == NULL
+    assert cascade(p, nn=4, kn=FAKE, vn=FAKE, sm=0) == NULL
+    assert cascade(p, nn=4, kn=FAKE + 8, vn=FAKE, sm=FAKE, q=0) == SHAPE  # misaligned rows, checked first
+    assert cascade(p, nn=4, kn=FAKE, vn=FAKE, sm=FAKE, q=0) == NULL  # valid rows: the next check decides
 
 
 def test_cascade_plan_and_workspace():
@@ -420,6 +426,17 @@ def test_check_cascade_validation():
     assert call(ng=-1) == SHAPE
     assert call(msh=-1) == SHAPE
     assert call(flags=FAKE + 2) == SHAPE
+
+
+def test_stream_read_validation():
+    lib = pa.load()
+    assert lib.pa_stream_read(FAKE, -16, FAKE, None) == SHAPE
+    assert lib.pa_stream_read(FAKE, 0, 0, None) == OK  # nothing to read: no-op
+    assert lib.pa_stream_read(0, 64, FAKE, None) == NULL
+    assert lib.pa_stream_read(FAKE, 64, 0, None) == NULL
+    assert lib.pa_stream_read(FAKE + 8, 64, FAKE, None) == SHAPE
+    assert lib.pa_stream_read(FAKE, 40, FAKE, None) == SHAPE
+    assert lib.pa_stream_read(FAKE, 64, FAKE + 2, None) == SHAPE
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):

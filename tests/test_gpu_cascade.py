@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import (assert_close, bits, f64, fresh, gpu_cascade, gpu_decode, named, oracle_whole,
+from gpu_helpers import (assert_close, bits, f64, fresh, gpu_cascade, gpu_decode, named, oracle_whole, pa,
                          stored_oracle_pools, torch)
 
 pytestmark = pytest.mark.gpu
@@ -210,3 +210,88 @@ def test_cascade_prefix_stage_beside_the_store():
         stage("combine")
         T.cuda.synchronize()
         assert bits(out) == whole
+
+
+# --------------------------------------------------------------------------
+# the step's new rows stored by the work-order launch
+# --------------------------------------------------------------------------
+def _cascade_with_rows(wl, dw, stage=None, out=None, ws=None, stream=None):
+    gs, ppt, shl, gmax, msh = cascade_device_cached(wl)
+    return pa().decode_cascade(dw.q, dw.k_pool, dw.v_pool, dw.page_table, dw.seq_lens, wl.max_seq_len, gs, gmax,
+                               ppt, shl, msh, wl.scale, out=out, workspace=ws, stage=stage, stream=stream,
+                               k_new=dw.k_new, v_new=dw.v_new, slot_mapping=dw.slot_mapping)
+
+
+_GROUPS = {}
+
+
+def cascade_device_cached(wl):
+    key = id(wl)
+    if key not in _GROUPS:
+        from gpu_helpers import cascade_device
+        _GROUPS[key] = cascade_device(wl)
+    return _GROUPS[key]
+
+
+def _assert_pools_stored(wl, dw):
+    kp, vp = stored_oracle_pools(wl)
+    assert W.to_numpy_storage(dw.k_pool, wl.dtype).tobytes() == kp.tobytes(), "K pool differs from the store"
+    assert W.to_numpy_storage(dw.v_pool, wl.dtype).tobytes() == vp.tobytes(), "V pool differs from the store"
+
+
+def test_cascade_stores_the_new_rows_on_the_radix_workload():
+    """One call stores the 256 new rows and attends them: pools bit-exact
+    against the oracle's store, every output element against the oracle;
+    the two-stream staged schedule gives the same bits."""
+    name = "qwen3_8b_radix"
+    banner(f"cascade with new rows {name}")
+    T = torch()
+    wl = W.make(name, poison="nan")
+    dw = W.to_device(wl)  # new rows not stored yet
+    out = _cascade_with_rows(wl, dw)
+    T.cuda.synchronize()
+    _assert_pools_stored(wl, dw)
+    err = assert_close(f64(out), oracle_whole(name), f"cascade with rows {name}")
+    # staged: prefix on a second stream from the start, the order-and-store
+    # launch, own keys and combine on the main stream, on fresh pools
+    dw2 = W.to_device(wl)
+    gs, ppt, shl, gmax, msh = cascade_device_cached(wl)
+    nb = pa().decode_cascade_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                             wl.max_seq_len, len(gs) - 1, gmax, msh)
+    ws = T.empty(nb, dtype=T.uint8, device="cuda")
+    out2 = T.empty_like(dw2.q)
+    side = T.cuda.Stream()
+    cur = T.cuda.current_stream()
+    side.wait_stream(cur)
+    with T.cuda.stream(side):
+        _cascade_with_rows(wl, dw2, stage="prefix", out=out2, ws=ws, stream=side)
+    for st in ("order", "suffix"):
+        _cascade_with_rows(wl, dw2, stage=st, out=out2, ws=ws)
+    cur.wait_stream(side)
+    _cascade_with_rows(wl, dw2, stage="combine", out=out2, ws=ws)
+    T.cuda.synchronize()
+    _assert_pools_stored(wl, dw2)
+    assert bits(out2) == bits(out), "staged schedule differs from the single call"
+    print(f"[result] cascade with rows {name}: pools exact, max abs err {err:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("case", ["small", "large"])
+def test_cascade_stores_rows_without_and_with_a_work_order(case):
+    """A batch too small for a work order (the launch only stores), and a
+    batch of more than 256 requests (1024-thread order work-group)."""
+    if case == "small":
+        lens, radix = [300, 200, 90, 400, 129, 40], (3, 8)
+    else:
+        rng = np.random.default_rng(77)
+        lens, radix = rng.integers(200, 1500, 640).tolist(), (16, 8)
+    banner(f"cascade with new rows, {case} batch: {len(lens)} requests")
+    # the large batch: 640 requests x 8 KV heads, work order of 10240 units
+    Hq, Hkv = (8, 2) if case == "small" else (32, 8)
+    wl = W.make_custom(lens, Hq, Hkv, 128, 16, dtype="bf16", radix=radix, seed=330)
+    dw = W.to_device(wl)
+    out = _cascade_with_rows(wl, dw)
+    torch().cuda.synchronize()
+    _assert_pools_stored(wl, dw)
+    kp, vp = stored_oracle_pools(wl)
+    ref = oracle.decode(wl.q, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    assert_close(f64(out), ref, f"cascade with rows, {case}")

@@ -89,3 +89,18 @@ def test_cascade_description_checks():
     # a request that shares nothing may sit in a group of its own
     sh2 = shl.copy(); sh2[2] = 0
     assert run(shl=sh2) == []
+
+
+def test_stream_read_calibration_reads_the_buffer():
+    banner("stream_read calibration")
+    T = torch()
+    src = T.arange(0, 1 << 20, dtype=T.int32, device="cuda")  # 4 MiB
+    sink = T.zeros(1, dtype=T.int32, device="cuda")
+    pa().stream_read(src, sink)
+    T.cuda.synchronize()
+    assert int(sink.item()) != 0
+    # a size that is not a whole number of grid strides
+    sink.zero_()
+    pa().stream_read(src[: (1 << 20) - 4 * 37], sink)
+    T.cuda.synchronize()
+    assert int(sink.item()) != 0

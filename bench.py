@@ -6,9 +6,10 @@ prefix sharing (256 requests, log-uniform lengths 512..8192, 32 query / 8 KV
 heads, head_dim 128, page 16, bf16; groups of 16 requests share a 1024-token
 prefix): the store of the 256 new K/V rows, then the cascade decode (shared
 prefix pass on the matrix cores, each request's own keys through the split-K
-decode kernel, combine).  The store and the own-keys pass's work order are
-one launch; the shared-prefix pass runs on a second stream beside it and the
-own-keys pass.  The same calls one after the other on one stream give the
+decode kernel, combine).  The work order and the own-keys pass follow the
+store on the caller's stream; the shared-prefix pass runs on a second stream
+beside them from the start of the step (it reads only shared pages, which the
+store does not write).  The same calls one after the other on one stream give the
 per-kernel times.  Inputs are resident in HBM before timing starts.
 The plain decode (partial + combine over every request's whole page list) and
 the chunked-prefill extend call (8 requests, prefix 0..4096 + 512-token
@@ -722,8 +723,8 @@ def main():
             "description": W.DESCRIPTIONS.get(args.config, args.config),
             "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
             "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "split_tokens": split,
-            "step": ("decode_cascade stages: the store of the 256 new rows and the work order in one launch, "
-                     "the own-keys pass, the prefix pass on a second stream beside them, then combine" if cascade
+            "step": ("kv_store of the 256 new rows, then the decode_cascade stages: the work order and the own-keys "
+                     "pass after the store, the prefix pass on a second stream beside them, then combine" if cascade
                      else "kv_store + decode_partial + decode_combine"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -18,13 +18,19 @@
 //  * GQA sharing.  The waves of a KV head serve all G query heads of it, so
 //    every K/V byte is fetched from HBM once per work unit and reused G times
 //    from registers.
-//  * Loads.  Each wave takes 16 keys per iteration.  K is read in a
-//    "quad" layout: four lanes per key, lane c holding 16-byte pieces
-//    c, c+4, ... of the key's head row; the QK dot product is a packed bf16
-//    dot (v_dot2_f32_bf16) plus a two-step DPP quad reduction.  V is read in
-//    a "row" layout: D/8 consecutive lanes cover one key's head row with
-//    16-byte loads, so each load instruction covers whole cache lines.
-//    Softmax weights move from the K layout to the V layout through LDS.
+//  * Loads.  Each wave takes 16 keys per iteration, and every load
+//    instruction covers whole 128-byte lines of the key rows.  K is read in
+//    an "octet" layout: eight lanes per key, lane o holding 16-byte pieces
+//    o, o+8, ... of the key's head row, keys a and a+8 for lane group a;
+//    the QK dot product is a packed bf16 dot (v_dot2_f32_bf16) plus a
+//    transposing three-step DPP reduction over the octet, after which each
+//    lane holds whole dot products of its own (key, head) pairs, so each
+//    score is exponentiated once.  (Read-only probes of the Qwen3-8B-shaped
+//    radix batch with nontemporal loads: 6.89 TB/s with K in octets against
+//    6.19 TB/s with four lanes per key, whose load instructions cover half
+//    lines.)  V is read in a "row" layout: D/8 consecutive lanes cover one
+//    key's head row with 16-byte loads.  Softmax weights move from the K
+//    layout to the V layout through LDS.
 //  * Online softmax with a wave-uniform reference maximum.  The reference is
 //    raised (and the accumulator rescaled) only when a score exceeds it by
 //    more than 2^8 in the exponent, so the common iteration does no cross-lane
@@ -52,12 +58,15 @@ template <bool BF16, int D, int G>
 struct DecodeCfg {
   static constexpr int EPC = BF16 ? 8 : 4;        // elements per 16-byte piece
   static constexpr int CPR = D / EPC;              // pieces per head row
-  static constexpr int NK = CPR / 4;               // K pieces per lane (quad layout)
+  static constexpr int PPL = CPR / 8;              // K pieces per lane and key (octet layout)
+  static constexpr int NK = 2 * PPL;               // K pieces per lane per iteration (two keys)
+  static constexpr int VP = (2 * G + 7) / 8 * 8;   // dot products per lane before the octet reduction
+  static constexpr int VPL = VP / 8;               // ... and after it
   static constexpr int LPR = CPR;                  // lanes per V row
   static constexpr int RPI = 64 / LPR;             // V rows per load instruction
   static constexpr int NV = kDecodeTokPerIter / RPI;  // V pieces per lane per iteration
   static constexpr int GP = (G + 3) & ~3;          // group padded for float4 LDS reads
-  static_assert(NK >= 1 && RPI >= 1 && NV >= 1, "bad tiling");
+  static_assert(PPL >= 1 && CPR % 8 == 0 && RPI >= 1 && NV >= 1, "bad tiling");
 };
 
 template <bool BF16, int D, int G>
@@ -120,7 +129,7 @@ struct DecodeOcc {
                                 : (BF16 && D == 128 && G == 4)  ? 5
                                 : (BF16 && D == 64 && G == 7)   ? 3
                                 : (D == 64 && G == 5)           ? 4
-                                : (!BF16 && D == 128 && G == 1) ? 6
+                                : (!BF16 && D == 128 && G == 1) ? 5
                                 : (!BF16 && D == 64 && G <= 3)  ? (G == 1 ? 8 : 7)
                                 : (!BF16 && D == 64 && G == 8)  ? 3
                                                                 : kEst;
@@ -180,6 +189,36 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_store_kernel(const P
     const int64_t dst = slot * s.row_chunks + c;
     k_pool[dst] = k_new[i];
     v_pool[dst] = v_new[i];
+  }
+}
+
+// Transposing sum over the eight lanes of each octet: value m of lane o
+// enters; afterwards lane o holds, at index u, the octet's sum of value
+// 8 u + o.  Each step pairs lanes that differ in one bit of o (partners
+// o ^ 7, o ^ 2, o ^ 1 in turn), keeps the half of the values whose index
+// bit matches that bit of the lane and receives the partner's copy of it.
+template <int VP>
+__device__ __forceinline__ void octet_reduce(float (&v)[VP], const int o) {
+  const bool b2 = (o & 4) != 0, b1 = (o & 2) != 0, b0 = (o & 1) != 0;
+  float w[VP / 2], x[VP / 4];
+#pragma unroll
+  for (int u = 0; u < VP / 8; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lo = v[8 * u + r], hi = v[8 * u + r + 4];
+      w[4 * u + r] = (b2 ? hi : lo) + octet_mirror(b2 ? lo : hi);
+    }
+#pragma unroll
+  for (int u = 0; u < VP / 8; ++u)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float lo = w[4 * u + r], hi = w[4 * u + r + 2];
+      x[2 * u + r] = (b1 ? hi : lo) + quad_xor2(b1 ? lo : hi);
+    }
+#pragma unroll
+  for (int u = 0; u < VP / 8; ++u) {
+    const float lo = x[2 * u], hi = x[2 * u + 1];
+    v[u] = (b0 ? hi : lo) + quad_xor1(b0 ? lo : hi);
   }
 }
 
@@ -291,8 +330,8 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
 
   // ---- the queries of the block's HB * G heads, staged in LDS (read back per
   // tile as broadcasts)
-  const int c = lane & 3;
-  const int tq = lane >> 2;  // key within the iteration (K layout)
+  const int o8 = lane & 7;   // piece column of the octet (K layout)
+  const int a8 = lane >> 3;  // keys a8 and a8 + 8 of the iteration (K layout)
   const int vr = lane / LPR;  // key row within a V load instruction
   const int vc = lane % LPR;  // 16-byte piece within the V row
   {
@@ -310,16 +349,32 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   const T* vbase = (const T*)p.v_pool + (int64_t)g * D;
   const float sl2 = p.scale_log2;
 
+  // the (key, head) pairs of this lane after the octet reduction: value
+  // m = 8 u + o8 is head m % G of key 8 (m / G) + a8 (m < 2 G; the rest pad)
+  constexpr int VP = C::VP, VPL = C::VPL, PPL = C::PPL;
+  // (recomputed where used: cheaper than holding them in registers)
+  auto live = [&](int u) __attribute__((always_inline)) { return 8 * u + o8 < 2 * G; };
+  auto h_of = [&](int u) __attribute__((always_inline)) { return live(u) ? (8 * u + o8) % G : 0; };
+  auto key_of = [&](int u) __attribute__((always_inline)) { return live(u) ? ((8 * u + o8) / G) * 8 + a8 : 0; };
+
   float m_ref[G];   // wave-uniform reference maximum (log2 domain)
-  float l_acc[G];   // per-lane partial sum of weights (K layout)
+  float l_acc[VPL];  // per-lane partial sum of weights of its pairs (K layout)
   float acc[G][EPC];  // per-lane partial output (V layout)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_ref[h] = -INFINITY;
-    l_acc[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
   }
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) l_acc[u] = 0.f;
+  // m_ref of this lane's head for pair u
+  auto ref_of = [&](int u) __attribute__((always_inline)) {
+    float r = m_ref[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) r = h_of(u) == h ? m_ref[h] : r;
+    return r;
+  };
 
   __syncthreads();  // s_slot and s_q ready
   if (t_begin < k0 || (int64_t)t_begin + n_tok > L) return;  // (work order only) uniform over the work-group
@@ -329,10 +384,13 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   // With no branch around the loads the compiler can keep DEPTH-1 tiles in
   // flight (a skipped load would force it to wait for every load).
   auto load_tile = [&](int ib, Tile<BF16, D, G>& tl) {
-    const int ik = min(ib + tq, n_tok - 1);
-    const T* kp = kbase + (int64_t)s_slot[ik] * row_stride;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) tl.k[j] = load16<NT>(kp + (c + 4 * j) * EPC);
+    for (int kg = 0; kg < 2; ++kg) {
+      const int ik = min(ib + 8 * kg + a8, n_tok - 1);
+      const T* kp = kbase + (int64_t)s_slot[ik] * row_stride;
+#pragma unroll
+      for (int pc = 0; pc < PPL; ++pc) tl.k[kg * PPL + pc] = load16<NT>(kp + (8 * pc + o8) * EPC);
+    }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int iv = min(ib + j * RPI + vr, n_tok - 1);
@@ -341,46 +399,53 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   };
 
   auto compute_tile = [&](int ib, const Tile<BF16, D, G>& tl) {
-    const bool valid = (ib + tq) < n_tok;
-    float sc[G];
+    // this lane's partial dot products (value kg * G + h: key 8 kg + a8,
+    // head h), then whole ones for its own pairs
+    float dv[VP];
 #pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = 0.f;
+    for (int m = 0; m < VP; ++m) dv[m] = 0.f;
 #pragma unroll
-    for (int j = 0; j < NK; ++j)
+    for (int pc = 0; pc < PPL; ++pc) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = dot_piece<BF16>(qw[h][c + 4 * j], tl.k[j], sc[h]);
+      for (int h = 0; h < G; ++h) {
+        const uint4 qv = qw[h][8 * pc + o8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = quad_sum(sc[h]);
-      sc[h] = valid ? a * sl2 : -INFINITY;
+        for (int kg = 0; kg < 2; ++kg) dv[kg * G + h] = dot_piece<BF16>(qv, tl.k[kg * PPL + pc], dv[kg * G + h]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one piece's queries in registers at a time
     }
+    octet_reduce<VP>(dv, o8);
+    float sc[VPL];
     bool over = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) over |= sc[h] > m_ref[h] + kRescaleSlack;
+    for (int u = 0; u < VPL; ++u) {
+      const bool valid = live(u) && ib + key_of(u) < n_tok;
+      sc[u] = valid ? dv[u] * sl2 : -INFINITY;
+      over |= sc[u] > ref_of(u) + kRescaleSlack;
+    }
     if (__ballot(over) != 0) {  // rare: raise the reference maximum
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mx = fmaxf(m_ref[h], wave_max(sc[h]));
+        float mh = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) mh = h_of(u) == h ? fmaxf(mh, sc[u]) : mh;
+        const float mx = fmaxf(m_ref[h], wave_max(mh));
         const float alpha = fast_exp2(m_ref[h] - mx);
         m_ref[h] = mx;
-        l_acc[h] *= alpha;
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) l_acc[u] = h_of(u) == h ? l_acc[u] * alpha : l_acc[u];
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha;
       }
     }
-    float pw[GP];
+    // each (key, head) weight is published by the one lane that holds it
+    float* sp = reinterpret_cast<float*>(&s_p4[wave][0][0]);
 #pragma unroll
-    for (int h = 0; h < GP; ++h) pw[h] = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      pw[h] = fast_exp2(sc[h] - m_ref[h]);
-      l_acc[h] += pw[h];
+    for (int u = 0; u < VPL; ++u) {
+      const float pw = live(u) ? fast_exp2(sc[u] - ref_of(u)) : 0.f;
+      l_acc[u] += pw;
+      if (live(u)) sp[key_of(u) * GP + h_of(u)] = pw;
     }
-    // lanes of a quad hold identical weights; lane c publishes heads c, c+4
-    float* sp = reinterpret_cast<float*>(&s_p4[wave][tq][0]);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      if ((h & 3) == c) sp[h] = pw[h];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -429,7 +494,12 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   // ---- reduce within the wave
   float l_w[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) l_w[h] = wave_sum(c == 0 ? l_acc[h] : 0.f);
+  for (int h = 0; h < G; ++h) {
+    float x = 0.f;
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) x += live(u) && h_of(u) == h ? l_acc[u] : 0.f;
+    l_w[h] = wave_sum(x);
+  }
 #pragma unroll
   for (int m = LPR; m < 64; m <<= 1)
 #pragma unroll

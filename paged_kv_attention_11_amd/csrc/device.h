@@ -42,6 +42,11 @@ __device__ __forceinline__ float quad_xor1(float x) {
 __device__ __forceinline__ float quad_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
+// DPP row half-mirror: value from lane 7 - i within each group of eight
+// lanes (that is, lane i ^ 7).
+__device__ __forceinline__ float octet_mirror(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+}
 // Sum over each group of four lanes; every lane of the group gets the sum.
 __device__ __forceinline__ float quad_sum(float x) {
   x += quad_xor1(x);

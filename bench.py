@@ -136,8 +136,7 @@ def read_ceiling(iters=10, nbytes=2 << 30):
 
     import paged_kv_attention_11_amd as pa
 
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    buf.fill_(1)
+    buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     ms = _time(torch, stream, lambda: pa.stream_read(buf, sink), iters)

@@ -556,7 +556,8 @@ pa_status pa_gather(const pa_kv_pool* pool, const int32_t* page_table, int32_t p
 
 /*
  * pa_stream_read: read `bytes` (a multiple of 16) of device memory at src
- * (16-byte aligned) with plain 16-byte vector loads and OR a nonzero digest
+ * (16-byte aligned) with nontemporal 16-byte vector loads (streamed past
+ * the caches; each work-group reads its own contiguous run) and OR a nonzero digest
  * of them into *sink (a uint32 in device memory; the value has no meaning
  * beyond keeping the loads live).  Calibration helper: the read-only HBM
  * rate this device reaches, the ceiling the streaming kernels (decode,

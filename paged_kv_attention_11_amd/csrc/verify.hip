@@ -13,7 +13,8 @@
 //    N dimension of 16x16 matrix-core tiles, two halves of 16 rows, so each
 //    K/V byte is read once for all of them.
 //  * K and V tiles of 64 keys come from the pages straight into an LDS ring
-//    (the extend kernel's pipeline).  Wave w takes row half w % 2 and head-dim
+//    (the extend kernel's pipeline), with nontemporal loads: each tile is
+//    read by one work-group only.  Wave w takes row half w % 2 and head-dim
 //    half w / 2: it computes the scores of its 16 rows over the whole tile,
 //    S^T = K Q^T with v_mfma_f32_16x16x32_bf16, and its half of their output,
 //    O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand (keys x
@@ -55,18 +56,23 @@ __device__ __forceinline__ f32x4_t mfma16_k16(const uint2& a, const uint2& b, co
 #define PA_VERIFY_STAGES 2
 #endif
 constexpr int kVStages = PA_VERIFY_STAGES;
+#ifndef PA_VERIFY_TILE
+#define PA_VERIFY_TILE 64
+#endif
+constexpr int kVT = PA_VERIFY_TILE;  // keys per tile
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   using C = ExtCfg<D>;
-  constexpr int PPR = C::PPR, NDMA = C::NDMA;
+  constexpr int PPR = C::PPR, NDMA = kVT * PPR / kThreads;  // DMA loads per thread per tile and tensor
+  static_assert(NDMA >= 1 && kVT * PPR % kThreads == 0 && kVT % 16 == 0, "bad tile");
   constexpr int KS = D / 32;           // 32-wide head-dim steps of S^T
   constexpr int DCW = D / 16 / 2;      // 16-wide output chunks per wave (half the head dims)
-  constexpr int NJ = kKT / 16;         // 16-key slices of a tile
+  constexpr int NJ = kVT / 16;         // 16-key slices of a tile
   static_assert(DCW >= 1, "head_dim too small");
 
-  __shared__ uint4 s_k[kVStages][kKT * PPR];
-  __shared__ uint4 s_v[kVStages][kKT * PPR];
+  __shared__ uint4 s_k[kVStages][kVT * PPR];
+  __shared__ uint4 s_v[kVStages][kVT * PPR];
   __shared__ int32_t s_pages[kPageCap];
 
   const int tid = threadIdx.x;
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   const int prefix = L - n;
   const int nq = min(n, p.max_q_len);  // rows computed (more than max_q_len breaks the contract)
   const int ns = (L + p.split_tokens - 1) / p.split_tokens;
-  const int ntiles = (k_end - k_begin + kKT - 1) / kKT;
+  const int ntiles = (k_end - k_begin + kVT - 1) / kVT;
 
   // ---- queries: row = i * G + h; this lane supplies row 16 rh + l16 of the
   // B operand, head dims 32 ks + 8 grp .. + 7
@@ -176,11 +182,11 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
     for (int m = 0; m < NDMA; ++m) {
       const int blk = wave * NDMA + m;
       const int key = blk * C::RPB + lane / PPR;
-      const int kk = min(k_begin + t * kKT + key, k_end - 1);
+      const int kk = min(k_begin + t * kVT + key, k_end - 1);
       const int32_t page = s_pages[(kk >> sh) - pg0];
       const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride;
-      dma16(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(key)) * 8);
-      dma16(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(key)) * 8);
+      dma16_nt(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(key)) * 8);
+      dma16_nt(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(key)) * 8);
     }
   };
 
@@ -216,8 +222,8 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
     }
 
     // ---- causal mask and the keys past the piece, on the last tiles only
-    const int kt0 = k_begin + t * kKT;
-    if (kt0 + kKT - 1 > prefix || kt0 + kKT > k_end) {
+    const int kt0 = k_begin + t * kVT;
+    if (kt0 + kVT - 1 > prefix || kt0 + kVT > k_end) {
       const int i = (rh * 16 + l16) / G;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)

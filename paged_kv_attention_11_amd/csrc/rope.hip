@@ -53,6 +53,16 @@ __device__ __forceinline__ uint4 pack(const float* f) {
   }
 }
 
+// Nontemporal 16-byte store (streamed past the caches): the rotated rows are
+// not read again by this kernel.  On the Qwen3-8B-shaped chunked-prefill
+// rows: 18.5 us against 19.4 us with cached stores; nontemporal loads of the
+// inputs (which the step producing them leaves in the caches) were slower,
+// 22.9 us.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(void* p, const uint4& v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), (u32x4_t*)p);
+}
+
 // Work item = (row, head slot, vector c of the first half).  Head slots
 // [0, Hq) rotate q, [Hq, Hq + Hkv) rotate k into the pool, [Hq + Hkv,
 // Hq + 2 Hkv) copy v into the pool.
@@ -77,8 +87,8 @@ __global__ __launch_bounds__(kThreads) void rope_store_kernel(const RopeArgs a) 
       const int hv = h - a.num_q_heads - a.num_kv_heads;
       const T* src = (const T*)a.v_new + (n * a.num_kv_heads + hv) * D;
       T* dst = (T*)a.v_pool + (slot * a.num_kv_heads + hv) * D;
-      *(uint4*)(dst + e0) = *(const uint4*)(src + e0);
-      *(uint4*)(dst + HALF + e0) = *(const uint4*)(src + HALF + e0);
+      store_nt(dst + e0, *(const uint4*)(src + e0));
+      store_nt(dst + HALF + e0, *(const uint4*)(src + HALF + e0));
       continue;
     }
     const T* src;
@@ -111,8 +121,8 @@ __global__ __launch_bounds__(kThreads) void rope_store_kernel(const RopeArgs a) 
       y0[k] = fmaf(x0[k], cs[k], -(x1[k] * sn[k]));
       y1[k] = fmaf(x1[k], cs[k], x0[k] * sn[k]);
     }
-    *(uint4*)(dst + e0) = pack<BF16>(y0);
-    *(uint4*)(dst + HALF + e0) = pack<BF16>(y1);
+    store_nt(dst + e0, pack<BF16>(y0));
+    store_nt(dst + HALF + e0, pack<BF16>(y1));
   }
 }
 

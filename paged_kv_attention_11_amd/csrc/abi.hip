@@ -52,6 +52,10 @@ using pa::kSplitQuantum;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+#ifndef PA_DECODE_CACHED_PIECES
+#define PA_DECODE_CACHED_PIECES 1
+#endif
+
 // Automatic split plan: the longest piece (a multiple of 64, at most
 // kMaxSplitTokens for decode, kVerifyMaxSplit for verify) that still gives
 // about kTargetUnits work-groups, i.e. two rounds of a full chip at the
@@ -228,6 +232,7 @@ pa_status prepare_decode(const pa_kv_pool* pool, const void* q, int32_t num_q_he
   a.group_piece_keys = 1;
   a.bf16 = pool->dtype == PA_BF16;
   a.scale_log2 = scale * kLog2e;
+  a.cached_keys = PA_DECODE_CACHED_PIECES < 0 ? INT_MAX : split * PA_DECODE_CACHED_PIECES;
   a.plan = workspace && use_plan(num_seqs, pool->num_kv_heads, S)
                ? (int4*)((char*)workspace + align256(rows * pool->head_dim * sizeof(float)) +
                          align256(rows * sizeof(float)))
@@ -654,6 +659,7 @@ pa_status cascade_impl(const pa_kv_pool* pool, const void* q, int32_t num_q_head
   a.heads_per_block = hb;
   a.group_lens = prefix_pass ? shared_lens : nullptr;
   a.group_piece_keys = pk;
+  a.cached_keys = 0;  // (the own keys are all read nontemporally)
   a.bf16 = 1;
   a.scale_log2 = scale * kLog2e;
   a.plan = use_plan(num_seqs, pool->num_kv_heads, S)

@@ -383,18 +383,20 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   // the piece's last key (a real row, so no NaN can enter; its weight is 0).
   // With no branch around the loads the compiler can keep DEPTH-1 tiles in
   // flight (a skipped load would force it to wait for every load).
-  auto load_tile = [&](int ib, Tile<BF16, D, G>& tl) {
+  // (nt: std::true_type for nontemporal loads)
+  auto load_tile = [&](int ib, Tile<BF16, D, G>& tl, auto nt) {
+    constexpr bool LNT = decltype(nt)::value;
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
       const int ik = min(ib + 8 * kg + a8, n_tok - 1);
       const T* kp = kbase + (int64_t)s_slot[ik] * row_stride;
 #pragma unroll
-      for (int pc = 0; pc < PPL; ++pc) tl.k[kg * PPL + pc] = load16<NT>(kp + (8 * pc + o8) * EPC);
+      for (int pc = 0; pc < PPL; ++pc) tl.k[kg * PPL + pc] = load16<LNT>(kp + (8 * pc + o8) * EPC);
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int iv = min(ib + j * RPI + vr, n_tok - 1);
-      tl.v[j] = load16<NT>(vbase + (int64_t)s_slot[iv] * row_stride + vc * EPC);
+      tl.v[j] = load16<LNT>(vbase + (int64_t)s_slot[iv] * row_stride + vc * EPC);
     }
   };
 
@@ -473,23 +475,31 @@ __global__ __launch_bounds__(kThreads, PA_DECODE_WAVES(BF16, D, G)) void decode_
   // ---- main loop: DEPTH tile buffers, DEPTH-1 tiles in flight while one is
   // computed (buffer indices are compile-time after unrolling)
   constexpr int kStep = WPH * kDecodeTokPerIter;
-  {
+  auto key_loop = [&](auto nt) {
     const int ib0 = ks * kDecodeTokPerIter;
     if (ib0 < n_tok) {  // uniform over the wave
       Tile<BF16, D, G> buf[DEPTH];
 #pragma unroll
-      for (int k = 0; k < DEPTH - 1; ++k) load_tile(ib0 + k * kStep, buf[k]);
+      for (int k = 0; k < DEPTH - 1; ++k) load_tile(ib0 + k * kStep, buf[k], nt);
       for (int base = ib0; base < n_tok; base += DEPTH * kStep) {
 #pragma unroll
         for (int k = 0; k < DEPTH; ++k) {
           const int cur = base + k * kStep;
           if (cur >= n_tok) break;
-          load_tile(cur + (DEPTH - 1) * kStep, buf[(k + DEPTH - 1) % DEPTH]);
+          load_tile(cur + (DEPTH - 1) * kStep, buf[(k + DEPTH - 1) % DEPTH], nt);
           compute_tile(cur, buf[k]);
         }
       }
     }
-  }
+  };
+  // Keys from cached_keys on are read nontemporally (all of them when NT):
+  // pages shared through a prefix cache are leading pages, which the other
+  // requests of a group read again, so the leading keys go through the caches
+  // and the rest streams past them.
+  if (NT || t_begin >= p.cached_keys)  // uniform over the work-group
+    key_loop(std::true_type{});
+  else
+    key_loop(std::false_type{});
 
   // ---- reduce within the wave
   float l_w[G];

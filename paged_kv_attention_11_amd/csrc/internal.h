@@ -97,6 +97,9 @@ struct DecodeArgs {
   int32_t ws_pieces;     // pieces per (request, head) row of the workspace
   int32_t always_partial;  // 1: never finish a single-piece request in the partial kernel
   int32_t heads_per_block;  // KV heads one work-group serves (1, 2 or 4; divides num_kv_heads)
+  // pieces starting at or after this key are read with nontemporal loads
+  // (the leading keys, which prefix caching shares, through the caches)
+  int32_t cached_keys;
   // leading pieces written by the shared-prefix kernel (combine only)
   const int32_t* group_lens;  // [B] keys covered by those pieces, or null
   int32_t group_piece_keys;

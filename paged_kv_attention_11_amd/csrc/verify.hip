@@ -61,18 +61,24 @@ constexpr int kVStages = PA_VERIFY_STAGES;
 #endif
 constexpr int kVT = PA_VERIFY_TILE;  // keys per tile
 
-template <int D, int G>
+// HP: KV heads per work-group (1 or 2).  With two, a tile holds half the
+// keys of both heads of the pair, row key * 2 + head (a key's two head slices
+// are 512 contiguous bytes of its pool row), and wave w serves head w / 2 over
+// all head dims instead of one head's half.
+template <int D, int G, int HP>
 __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   using C = ExtCfg<D>;
-  constexpr int PPR = C::PPR, NDMA = kVT * PPR / kThreads;  // DMA loads per thread per tile and tensor
-  static_assert(NDMA >= 1 && kVT * PPR % kThreads == 0 && kVT % 16 == 0, "bad tile");
+  constexpr int VT = kVT / HP;         // keys per tile
+  constexpr int TR = VT * HP;          // tile rows: (key, head) pairs
+  constexpr int PPR = C::PPR, NDMA = TR * PPR / kThreads;  // DMA loads per thread per tile and tensor
+  static_assert(NDMA >= 1 && TR * PPR % kThreads == 0 && VT % 16 == 0, "bad tile");
   constexpr int KS = D / 32;           // 32-wide head-dim steps of S^T
-  constexpr int DCW = D / 16 / 2;      // 16-wide output chunks per wave (half the head dims)
-  constexpr int NJ = kVT / 16;         // 16-key slices of a tile
-  static_assert(DCW >= 1, "head_dim too small");
+  constexpr int DCW = D / 16 * HP / 2;  // 16-wide output chunks per wave
+  constexpr int NJ = VT / 16;          // 16-key slices of a tile
+  static_assert(DCW >= 1 && (HP == 1 || HP == 2), "bad shape");
 
-  __shared__ uint4 s_k[kVStages][kVT * PPR];
-  __shared__ uint4 s_v[kVStages][kVT * PPR];
+  __shared__ uint4 s_k[kVStages][TR * PPR];
+  __shared__ uint4 s_v[kVStages][TR * PPR];
   __shared__ int32_t s_pages[kPageCap];
 
   const int tid = threadIdx.x;
@@ -80,8 +86,9 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  const int rh = wave & 1;   // row half: rows 16 rh .. 16 rh + 15
-  const int dg = wave >> 1;  // head-dim half of the output
+  const int rh = wave & 1;                 // row half: rows 16 rh .. 16 rh + 15
+  const int dg = HP == 1 ? wave >> 1 : 0;  // head-dim half of the output (one head per work-group)
+  const int hh = HP == 1 ? 0 : wave >> 1;  // head of the pair (two per work-group)
 
   // work-group -> (piece s, request b, KV head g).  Pieces are taken piece
   // index slowest; the KV head is fastest, so each XCD (work-group i runs on
@@ -94,8 +101,10 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   // more pieces that tail of empty work-groups grows long enough to cost
   // more than it saves (256-key pieces: 211 -> 245 us), and the plain order
   // is kept.
-  const int g = blockIdx.x % p.num_kv_heads;
-  const int pos = blockIdx.x / p.num_kv_heads;
+  const int nhb = p.num_kv_heads / HP;
+  const int gb = blockIdx.x % nhb;  // head block: heads gb * HP .. + HP - 1
+  const int g = gb * HP + hh;       // this wave's KV head
+  const int pos = blockIdx.x / nhb;
   int s, b;
   if (p.num_seqs <= 64 && p.max_splits <= 8) {
     int ns = 0;  // lane j: pieces of request j
@@ -136,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   const int prefix = L - n;
   const int nq = min(n, p.max_q_len);  // rows computed (more than max_q_len breaks the contract)
   const int ns = (L + p.split_tokens - 1) / p.split_tokens;
-  const int ntiles = (k_end - k_begin + kVT - 1) / kVT;
+  const int ntiles = (k_end - k_begin + VT - 1) / VT;
 
   // ---- queries: row = i * G + h; this lane supplies row 16 rh + l16 of the
   // B operand, head dims 32 ks + 8 grp .. + 7
@@ -171,8 +180,8 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   __syncthreads();
 
   const int64_t row_stride = (int64_t)p.num_kv_heads * D;
-  const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)g * D;
-  const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)g * D;
+  const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)gb * HP * D;  // the block's first head
+  const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)gb * HP * D;
 
   // DMA of tile t into ring slot sb; keys past the piece are clamped to its
   // last key (a real row, masked out of the softmax)
@@ -181,12 +190,12 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
 #pragma unroll
     for (int m = 0; m < NDMA; ++m) {
       const int blk = wave * NDMA + m;
-      const int key = blk * C::RPB + lane / PPR;
-      const int kk = min(k_begin + t * kVT + key, k_end - 1);
+      const int row = blk * C::RPB + lane / PPR;  // (key, head) pair of the tile
+      const int kk = min(k_begin + t * VT + row / HP, k_end - 1);
       const int32_t page = s_pages[(kk >> sh) - pg0];
-      const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride;
-      dma16_nt(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(key)) * 8);
-      dma16_nt(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(key)) * 8);
+      const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride + (row % HP) * D;
+      dma16_nt(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(row)) * 8);
+      dma16_nt(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(row)) * 8);
     }
   };
 
@@ -213,17 +222,17 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       sacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int key_l = 16 * j + l16;
+      const int row_l = (16 * j + l16) * HP + hh;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = s_k[buf][key_l * PPR + ((4 * ks + grp) ^ k_swz<D>(key_l))];
+        const uint4 a = s_k[buf][row_l * PPR + ((4 * ks + grp) ^ k_swz<D>(row_l))];
         sacc[j] = mfma16_k32(a, qreg[ks], sacc[j]);
       }
     }
 
     // ---- causal mask and the keys past the piece, on the last tiles only
-    const int kt0 = k_begin + t * kVT;
-    if (kt0 + kVT - 1 > prefix || kt0 + kVT > k_end) {
+    const int kt0 = k_begin + t * VT;
+    if (kt0 + VT - 1 > prefix || kt0 + VT > k_end) {
       const int i = (rh * 16 + l16) / G;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
         const int within = (d & 4) ? 8 : 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int kr = 16 * j + 4 * grp + (l16 >> 2);
+          const int kr = (16 * j + 4 * grp + (l16 >> 2)) * HP + hh;  // tile row of the key for this head
           const uint2 x = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
           o[c] = mfma16_k16(x, pb[j], o[c]);
         }
@@ -379,11 +388,19 @@ __global__ __launch_bounds__(256) void verify_combine_kernel(const VerifyArgs p)
   for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(o[e]);
 }
 
+#ifndef PA_VERIFY_HEAD_PAIRS
+#define PA_VERIFY_HEAD_PAIRS 1
+#endif
+
 template <int D, int G>
 hipError_t launch_g(const VerifyArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.num_seqs * a.num_kv_heads * a.max_splits;
+  const bool pairs = PA_VERIFY_HEAD_PAIRS && a.num_kv_heads % 2 == 0;
+  const int64_t blocks = (int64_t)a.num_seqs * (a.num_kv_heads / (pairs ? 2 : 1)) * a.max_splits;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((verify_kernel<D, G>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  if (pairs)
+    hipLaunchKernelGGL((verify_kernel<D, G, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((verify_kernel<D, G, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits <= 1) return e;
   const int64_t rows = (int64_t)a.num_seqs * a.max_q_len * a.num_q_heads;

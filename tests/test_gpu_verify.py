@@ -37,6 +37,8 @@ VERIFY_SWEEP = [
     ([900, 1200], [6, 6], 40, 8, 128, 16, 128),                                 # group 5: 30 rows
     ([77, 2100, 640], [6, 3, 6], 24, 8, 128, 16, 0),                            # group 3
     ([1500, 70], [5, 5], 12, 2, 128, 1, 256),                                   # group 6, page size 1
+    ([800, 50, 3100], [6, 6, 2], 12, 3, 128, 16, 0),                            # odd KV heads: one per work-group
+    ([400, 2000], [3, 4], 8, 1, 64, 16, 256),                                   # one KV head, group 8, D = 64
 ]
 
 

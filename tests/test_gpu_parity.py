@@ -138,6 +138,9 @@ DECODE_SWEEP = [
     ([0, 5, 0, 40], 8, 2, 128, 16, "bf16", 0),          # empty requests
     ([4097], 32, 8, 128, 16, "bf16", 0),                # one long request
     ([1, 2047, 2048, 2049, 4097], 32, 8, 128, 16, "bf16", 2048),  # largest pieces
+    ([300, 1500, 2100], 8, 8, 128, 16, "f32", 0),       # fp32, group 1 x 128 (octet reduction padded)
+    ([65, 700, 1300], 6, 2, 64, 16, "f32", 128),        # fp32, group 3 x 64
+    ([900, 1800, 40], 56, 8, 128, 16, "bf16", 0),       # group 7 x 128
 ]
 
 

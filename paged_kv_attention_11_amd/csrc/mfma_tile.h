@@ -68,51 +68,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
 }
 
 // Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
-// lane i's 16 bytes land at LDS address `lds` + 16 i.  Issued as inline asm so
-// the compiler's wait-count pass does not serialise it against unrelated LDS
-// reads; completion is awaited explicitly with vm_wait below.
-__device__ __forceinline__ void dma16(uint32_t lds, const void* gptr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
-}
-// The same load, nontemporal (streamed past the caches): for tiles that no
-// other work-group reads again.  On the Qwen3-8B-shaped verify workload
-// 154 us against 167 us with the cached form; the extend kernel, whose
-// work-groups of one (request, KV head) read the same tiles from L2, keeps
-// the cached form (213 against 229 us).
-__device__ __forceinline__ void dma16_nt(uint32_t lds, const void* gptr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(gptr) : "memory", "m0");
-}
-// The cached load without a memory clobber, so that the compiler may move
-// ordinary LDS reads across it.  For rings whose slots being filled are never
-// read before the next barrier; ordering against the waits and barriers is
-// kept (both are volatile).
+// lane i's 16 bytes land at LDS address `lds` + 16 i.  Issued as inline asm
+// without a memory clobber, so that the compiler's wait-count pass does not
+// serialise it against unrelated LDS reads and may move ordinary LDS reads
+// across it: for rings whose slots being filled are never read before the
+// next barrier.  Completion is awaited explicitly with vm_wait below;
+// ordering against the waits and barriers is kept (both are volatile).
 __device__ __forceinline__ void dma16_unordered(uint32_t lds, const void* gptr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "m0");
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until the next tile of an S-stage ring has landed while the `after`
-// tiles issued behind it (at most S - 2; fewer near the end) stay in flight.
-// NDMA: direct-to-LDS loads per thread per tile and tensor (K and V: 2 NDMA).
-template <int S, int NDMA>
-__device__ __forceinline__ void wait_next(int after) {
-  static_assert(S >= 2 && S <= 4, "ring depth");
-  if constexpr (S >= 4) {
-    if (after >= 2) {
-      vm_wait<4 * NDMA>();
-      return;
-    }
-  }
-  if constexpr (S >= 3) {
-    if (after >= 1) {
-      vm_wait<2 * NDMA>();
-      return;
-    }
-  }
-  vm_wait<0>();
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));

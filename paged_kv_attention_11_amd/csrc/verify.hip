@@ -7,23 +7,26 @@
 //
 // Design:
 //  * Split-K like decode: work-group = (piece s of split_tokens keys,
-//    request b, KV head g), piece index slowest; the pieces are merged by
-//    verify_combine_kernel with log-sum-exp weights.
-//  * The n rows x G query heads of (b, g) (at most 32) are packed into the
-//    N dimension of 16x16 matrix-core tiles, two halves of 16 rows, so each
-//    K/V byte is read once for all of them.
-//  * K and V tiles of 64 keys come from the pages straight into an LDS ring
-//    (the extend kernel's pipeline), with nontemporal loads: each tile is
-//    read by one work-group only.  Wave w takes row half w % 2 and head-dim
-//    half w / 2: it computes the scores of its 16 rows over the whole tile,
-//    S^T = K Q^T with v_mfma_f32_16x16x32_bf16, and its half of their output,
+//    request b, KV head or pair of KV heads); the pieces are merged by
+//    verify_combine_kernel with log-sum-exp weights.  Pieces are dispatched
+//    longest first (longest_first_piece).
+//  * The n rows x G query heads of (b, g) (at most 32, row = i G + h) are
+//    the N dimension of two 16-row matrix-core tiles, so each K/V byte is
+//    read once for all of them: S^T = K Q^T with v_mfma_f32_16x16x32_bf16,
 //    O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand (keys x
 //    rows) is exactly the score accumulator's layout, so P never leaves
-//    registers; V^T is read with the transposing LDS read.
-//  * The two waves of a row half hold identical running maxima and sums and
-//    disjoint output columns: nothing is merged between waves at the end.
-//  * Row (token i, head h) sees keys <= L - n + i; only the tiles that reach
-//    past L - n are masked.
+//    registers.
+//  * Each wave streams its own 32-key chunks of the piece (chunk c to wave
+//    c mod W of the head's W waves) with its own online softmax; the W
+//    partial results of a head are merged through LDS at the end, so the key
+//    loop has no work-group barrier.  A chunk's K and V rows are loaded whole
+//    (16-byte pieces, a load instruction covering four 256-byte rows) into
+//    registers with nontemporal loads one chunk ahead, written to the wave's
+//    own LDS slot and read back in the operand layouts (V^T with the
+//    transposing LDS read).  Within a wave the slot needs no barrier: a
+//    wave's LDS instructions execute in the order it issues them.
+//  * Row (token i, head h) sees keys <= L - n + i; only the chunks that
+//    reach past L - n are masked.
 #include "device.h"
 #include "internal.h"
 #include "mfma_tile.h"
@@ -48,90 +51,95 @@ __device__ __forceinline__ f32x4_t mfma16_k16(const uint2& a, const uint2& b, co
                                                    c, 0, 0, 0);
 }
 
-// LDS ring depth: kVStages - 1 tiles in flight per work-group.  Two stages
-// (64 KB for D = 128) let two work-groups share a compute unit, which hides
-// more latency than a third stage in one work-group (190 vs 237 us on the
-// Qwen3-8B-shaped verify workload).
-#ifndef PA_VERIFY_STAGES
-#define PA_VERIFY_STAGES 2
-#endif
-constexpr int kVStages = PA_VERIFY_STAGES;
-#ifndef PA_VERIFY_TILE
-#define PA_VERIFY_TILE 64
-#endif
-constexpr int kVT = PA_VERIFY_TILE;  // keys per tile
+// Longest-first work order for batches of at most 64 requests: position
+// `pos` of a KV-head block takes every full piece (split_tokens keys) first,
+// piece index slowest, then the shorter last pieces by decreasing key count
+// (ties in request order).  Returns false past the last existing piece: the
+// grid covers every possible piece (max_splits per request), and the
+// work-groups with nothing to do all come at the end of the dispatch order
+// instead of holding slots between the others.  On the Qwen3-8B-shaped
+// verify workload (64 requests, 1024-key pieces) 135-140 us in this order
+// against 148-154 us with the existing pieces taken piece index slowest
+// regardless of length.  Lane j holds request j; every lane of the wave
+// calls this.
+__device__ __forceinline__ bool longest_first_piece(const VerifyArgs& p, int pos, int lane, int& s, int& b) {
+  int nfull = 0, rem = -1;
+  if (lane < p.num_seqs && p.q_indptr[lane + 1] - p.q_indptr[lane] > 0) {
+    const int lj = p.seq_lens[lane];
+    nfull = lj / p.split_tokens;
+    rem = lj - nfull * p.split_tokens;
+    if (rem == 0) rem = -1;  // no shorter last piece
+  }
+  s = -1;
+  b = 0;
+  int before = 0;  // full pieces of the lower piece indices
+  for (int sp = 0; sp < p.max_splits; ++sp) {  // uniform loop
+    const uint64_t have = __ballot(nfull > sp);
+    const int c = __popcll(have);
+    if (c == 0) break;
+    if (pos < before + c) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(have >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)have, 0u));
+      s = sp;
+      b = __builtin_ctzll(__ballot(nfull > sp && below == pos - before));
+      break;
+    }
+    before += c;
+  }
+  if (s < 0) {
+    const int q = pos - before;  // rank among the last pieces
+    int rank = 0;                // this lane's rank
+    for (int i = 0; i < p.num_seqs; ++i) {  // uniform loop
+      const int ri = __builtin_amdgcn_readlane(rem, i);
+      rank += (ri > rem || (ri == rem && i < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(rem >= 0 && rank == q);
+    if (hit == 0) return false;  // uniform: past the last existing piece
+    b = __builtin_ctzll(hit);
+    s = __builtin_amdgcn_readlane(nfull, b);
+  }
+  return true;
+}
 
-// HP: KV heads per work-group (1 or 2).  With two, a tile holds half the
-// keys of both heads of the pair, row key * 2 + head (a key's two head slices
-// are 512 contiguous bytes of its pool row), and wave w serves head w / 2 over
-// all head dims instead of one head's half.
+// HP: KV heads per work-group (1 or 2): the four waves serve HP heads, 4 / HP
+// waves each, so with two the loads of a key's two head slices (512
+// contiguous bytes of its pool row) are issued at about the same time.
 template <int D, int G, int HP>
-__global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
+__global__ __launch_bounds__(kThreads, 2) void verify_kernel(const VerifyArgs p) {
   using C = ExtCfg<D>;
-  constexpr int VT = kVT / HP;         // keys per tile
-  constexpr int TR = VT * HP;          // tile rows: (key, head) pairs
-  constexpr int PPR = C::PPR, NDMA = TR * PPR / kThreads;  // DMA loads per thread per tile and tensor
-  static_assert(NDMA >= 1 && TR * PPR % kThreads == 0 && VT % 16 == 0, "bad tile");
-  constexpr int KS = D / 32;           // 32-wide head-dim steps of S^T
-  constexpr int DCW = D / 16 * HP / 2;  // 16-wide output chunks per wave
-  constexpr int NJ = VT / 16;          // 16-key slices of a tile
-  static_assert(DCW >= 1 && (HP == 1 || HP == 2), "bad shape");
+  constexpr int PPR = C::PPR;
+  constexpr int KS = D / 32;         // k-steps of S^T
+  constexpr int DC = D / 16;         // 16-wide head-dim tiles of O^T
+  constexpr int WPH = 4 / HP;        // waves per KV head
+  constexpr int CK = 32;             // keys per chunk
+  constexpr int KPL = 64 / PPR;      // keys per load instruction (whole rows)
+  constexpr int NV = CK / KPL;       // K (and V) loads per lane per chunk
+  constexpr int SLOT = 2 * CK * PPR;  // uint4 per wave: a K and a V chunk, or its O^T (32 rows x D fp32) at the end
+  static_assert(HP == 1 || HP == 2, "bad shape");
+  static_assert(SLOT * 16 == 32 * D * 4, "slot holds a wave's O^T");
 
-  __shared__ uint4 s_k[kVStages][TR * PPR];
-  __shared__ uint4 s_v[kVStages][TR * PPR];
+  __shared__ uint4 s_buf[kThreads / 64][SLOT];
   __shared__ int32_t s_pages[kPageCap];
+  __shared__ float s_m[kThreads / 64][32];
+  __shared__ float s_l[kThreads / 64][32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  const int rh = wave & 1;                 // row half: rows 16 rh .. 16 rh + 15
-  const int dg = HP == 1 ? wave >> 1 : 0;  // head-dim half of the output (one head per work-group)
-  const int hh = HP == 1 ? 0 : wave >> 1;  // head of the pair (two per work-group)
+  const int hh = wave / WPH;  // head of the block
+  const int sw = wave % WPH;  // this wave's share of the chunks
 
-  // work-group -> (piece s, request b, KV head g).  Pieces are taken piece
-  // index slowest; the KV head is fastest, so each XCD (work-group i runs on
-  // XCD i mod 8) gets the same share of every piece.  In a batch of at most
-  // 64 requests split into at most 8 pieces, work-group p of a head takes
-  // the p-th piece that exists (requests are of different lengths, so later
-  // piece indices exist for fewer of them): the work-groups with nothing to
-  // do come last in the dispatch order instead of holding slots between the
-  // others (181 -> 168 us on the Qwen3-8B-shaped verify workload).  With
-  // more pieces that tail of empty work-groups grows long enough to cost
-  // more than it saves (256-key pieces: 211 -> 245 us), and the plain order
-  // is kept.
+  // work-group -> (piece s, request b, KV head block); the KV head block is
+  // the fastest index, so each XCD gets the same share of every piece
   const int nhb = p.num_kv_heads / HP;
-  const int gb = blockIdx.x % nhb;  // head block: heads gb * HP .. + HP - 1
-  const int g = gb * HP + hh;       // this wave's KV head
+  const int gb = blockIdx.x % nhb;
+  const int g = gb * HP + hh;
   const int pos = blockIdx.x / nhb;
   int s, b;
-  if (p.num_seqs <= 64 && p.max_splits <= 8) {
-    int ns = 0;  // lane j: pieces of request j
-    if (lane < p.num_seqs) {
-      const int nj = p.q_indptr[lane + 1] - p.q_indptr[lane];
-      const int lj = p.seq_lens[lane];
-      ns = nj > 0 ? (lj + p.split_tokens - 1) / p.split_tokens : 0;
-    }
-    s = -1;
-    b = 0;
-    int before = 0;  // existing pieces of the lower piece indices
-    for (int sp = 0; sp < p.max_splits; ++sp) {  // uniform loop
-      const bool has = ns > sp;
-      const uint64_t have = __ballot(has);
-      const int c = __popcll(have);
-      if (pos < before + c) {
-        // the request whose piece sp is the (pos - before)-th that exists:
-        // the lane with that many existing pieces below it
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(have >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)have, 0u));
-        s = sp;
-        b = __builtin_ctzll(__ballot(has && below == pos - before));
-        break;
-      }
-      before += c;
-    }
-    if (s < 0) return;  // uniform: past the last existing piece
+  if (p.num_seqs <= 64) {
+    if (!longest_first_piece(p, pos, lane, s, b)) return;  // uniform
   } else {
     s = pos / p.num_seqs;
     b = pos - s * p.num_seqs;
@@ -143,32 +151,34 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   if (n <= 0 || k_begin >= L) return;  // uniform over the work-group
   const int k_end = min(k_begin + p.split_tokens, L);
   const int prefix = L - n;
-  const int nq = min(n, p.max_q_len);  // rows computed (more than max_q_len breaks the contract)
+  const int nq = min(n, p.max_q_len);
   const int ns = (L + p.split_tokens - 1) / p.split_tokens;
-  const int ntiles = (k_end - k_begin + VT - 1) / VT;
+  const int nch = (k_end - k_begin + CK - 1) / CK;
 
-  // ---- queries: row = i * G + h; this lane supplies row 16 rh + l16 of the
-  // B operand, head dims 32 ks + 8 grp .. + 7
-  uint4 qreg[KS];
-  {
-    const int row = rh * 16 + l16;
+  // ---- queries: row = i * G + h in two 16-row tiles; this lane supplies row
+  // 16 rt + l16 of tile rt's B operand, head dims 32 ks + 8 grp .. + 7
+  uint4 qreg[2][KS];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = rt * 16 + l16;
     const int i = row / G, h = row % G;
     const bool ok = i < nq;
     const uint16_t* qp =
         (const uint16_t*)p.q + ((int64_t)(r0 + (ok ? i : 0)) * p.num_q_heads + (int64_t)g * G + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qreg[ks] = ok ? *(const uint4*)(qp + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
+      qreg[rt][ks] = ok ? *(const uint4*)(qp + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
   }
-  // retire the query loads once, so the key loop carries no wait for them
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4_t v = __builtin_bit_cast(u32x4_t, qreg[ks]);
-    asm volatile("" : "+v"(v));
-    qreg[ks] = __builtin_bit_cast(uint4, v);
-  }
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t v = __builtin_bit_cast(u32x4_t, qreg[rt][ks]);
+      asm volatile("" : "+v"(v));
+      qreg[rt][ks] = __builtin_bit_cast(uint4, v);
+    }
 
-  // ---- page ids of the piece (split_tokens <= 1024 keys: at most 1024 pages)
+  // ---- page ids of the piece (at most 1024 keys: at most 1024 pages)
   const int sh = p.log2_page;
   const int pmask = (1 << sh) - 1;
   const int pg0 = k_begin >> sh;
@@ -179,151 +189,202 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs p) {
   }
   __syncthreads();
 
-  const int64_t row_stride = (int64_t)p.num_kv_heads * D;
-  const uint16_t* kbase = (const uint16_t*)p.k_pool + (int64_t)gb * HP * D;  // the block's first head
-  const uint16_t* vbase = (const uint16_t*)p.v_pool + (int64_t)gb * HP * D;
-
-  // DMA of tile t into ring slot sb; keys past the piece are clamped to its
+  const uint32_t row_bytes = (uint32_t)p.num_kv_heads * D * 2u;
+  const char* const kb8 = (const char*)p.k_pool + (int64_t)g * D * 2;
+  const char* const vb8 = (const char*)p.v_pool + (int64_t)g * D * 2;
+  // byte offset of a key's pool row; keys past the piece are clamped to its
   // last key (a real row, masked out of the softmax)
-  auto issue_tile = [&](int t, int sb) {
-    const int pc = lane % PPR;
+  auto row_off = [&](int key) __attribute__((always_inline)) {
+    const int kk = min(key, k_end - 1);
+    const int32_t page = s_pages[(kk >> sh) - pg0];
+    return (uint64_t)(uint32_t)((page << sh) | (kk & pmask)) * row_bytes;
+  };
+  // Chunk c's K and V, whole rows: load m covers keys m KPL .. + KPL - 1, lane
+  // l piece l % PPR of key m KPL + l / PPR.  Past the wave's last chunk every
+  // key clamps to the piece's last key: the loads are issued anyway (one row,
+  // the values never used), so that no load sits under a branch -- the
+  // compiler's waits would then also count the next chunk's loads.
+  uint4 kreg[NV], vreg[NV];
+  auto load_kv = [&](int c) __attribute__((always_inline)) {
+    const int kb = k_begin + c * CK;
 #pragma unroll
-    for (int m = 0; m < NDMA; ++m) {
-      const int blk = wave * NDMA + m;
-      const int row = blk * C::RPB + lane / PPR;  // (key, head) pair of the tile
-      const int kk = min(k_begin + t * VT + row / HP, k_end - 1);
-      const int32_t page = s_pages[(kk >> sh) - pg0];
-      const int64_t off = ((int64_t)((page << sh) | (kk & pmask))) * row_stride + (row % HP) * D;
-      dma16_nt(lds_addr(&s_k[sb][blk * 64]), kbase + off + (pc ^ k_swz<D>(row)) * 8);
-      dma16_nt(lds_addr(&s_v[sb][blk * 64]), vbase + off + (pc ^ v_swz<D>(row)) * 8);
+    for (int m = 0; m < NV; ++m) {
+      const uint64_t off = row_off(kb + m * KPL + lane / PPR) + 16 * (lane % PPR);
+      kreg[m] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)(kb8 + off)));
+      vreg[m] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)(vb8 + off)));
     }
   };
+  // the wave's LDS slot: K rows (pieces XOR key mod PPR), then V rows
+  uint4* const kslot = &s_buf[wave][0];
+  uint4* const slot = &s_buf[wave][CK * PPR];
 
-  f32x4_t o[DCW];  // O^T chunk dc = dg * DCW + c: lane holds d = 16 dc + 4 grp + r, row 16 rh + l16
+  f32x4_t o[DC][2];  // O^T tile (dc, rt): lane holds d = 16 dc + 4 grp + r of row 16 rt + l16
 #pragma unroll
-  for (int c = 0; c < DCW; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // raw-score reference maximum of this lane's row
-  float l_run = 0.f;        // this lane's part of the row sum
+  for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) o[dc][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {-INFINITY, -INFINITY};  // raw-score reference maximum of this lane's rows
+  float l_run[2] = {0.f, 0.f};              // this lane's part of the row sums
   const float sl2 = p.scale_log2;
   const float slack = kSlack / sl2;
 
-  // ---- prologue: tiles 0 .. kVStages - 2 in flight, tile 0 landed
-  for (int t = 0; t < kVStages - 1 && t < ntiles; ++t) issue_tile(t, t);
-  wait_next<kVStages, NDMA>(min(kVStages - 2, ntiles - 1));
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t % kVStages;
-    if (t + kVStages - 1 < ntiles) issue_tile(t + kVStages - 1, (t + kVStages - 1) % kVStages);
-
-    // ---- S^T of the whole tile for this row half: slice j, lane holds keys
-    // 16 j + 4 grp + r of row 16 rh + l16
-    f32x4_t sacc[NJ];
+  load_kv(sw);
+  for (int c = sw; c < nch; c += WPH) {
+    // this chunk into the wave's slot, row = key, swizzled as the reads below
+    // expect
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      sacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int row_l = (16 * j + l16) * HP + hh;
+    for (int m = 0; m < NV; ++m) {
+      const int kr = m * KPL + lane / PPR;
+      kslot[kr * PPR + ((lane % PPR) ^ k_swz<D>(kr))] = kreg[m];
+      slot[kr * PPR + ((lane % PPR) ^ v_swz<D>(kr))] = vreg[m];
+    }
+    load_kv(c + WPH);  // the next chunk of this wave, loaded meanwhile
+    asm volatile("" ::: "memory");  // the slot's stores stay before its reads
+
+    // ---- S^T: tile (j, rt), lane holds keys 16 j + 4 grp + r of row 16 rt + l16
+    f32x4_t sacc[2][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = s_k[buf][row_l * PPR + ((4 * ks + grp) ^ k_swz<D>(row_l))];
-        sacc[j] = mfma16_k32(a, qreg[ks], sacc[j]);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        sacc[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int kr = 16 * j + l16;
+          sacc[j][rt] = mfma16_k32(kslot[kr * PPR + ((4 * ks + grp) ^ k_swz<D>(kr))], qreg[rt][ks], sacc[j][rt]);
+        }
+      }
+
+    // ---- causal mask and the keys past the piece, on the last chunks only
+    const int kt0 = k_begin + c * CK;
+    if (kt0 + CK - 1 > prefix || kt0 + CK > k_end) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int i = (rt * 16 + l16) / G;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kt0 + 16 * j + 4 * grp + r;
+            if (key > prefix + i || key >= k_end) sacc[j][rt][r] = -INFINITY;
+          }
       }
     }
 
-    // ---- causal mask and the keys past the piece, on the last tiles only
-    const int kt0 = k_begin + t * VT;
-    if (kt0 + VT - 1 > prefix || kt0 + VT > k_end) {
-      const int i = (rh * 16 + l16) / G;
+    // ---- online softmax per row tile; the four lane groups hold the row's keys
+    uint2 pb[2][2];  // P^T B operands: keys 16 j + 4 grp .. + 3 of row 16 rt + l16
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+    for (int rt = 0; rt < 2; ++rt) {
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][rt][0], sacc[0][rt][1]), fmaxf(sacc[0][rt][2], sacc[0][rt][3])),
+                       fmaxf(fmaxf(sacc[1][rt][0], sacc[1][rt][1]), fmaxf(sacc[1][rt][2], sacc[1][rt][3])));
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      if (__ballot(mx > m_ref[rt] + slack) != 0) {
+        const float m_new = fmaxf(m_ref[rt], mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref[rt] - m_new) * sl2);
+        m_ref[rt] = m_new;
+        l_run[rt] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt0 + 16 * j + 4 * grp + r;
-          if (key > prefix + i || key >= k_end) sacc[j][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax: row maximum over this lane's keys and the lanes
-    // holding the same row (lane ^ 16, lane ^ 32)
-    float mx = -INFINITY;
+        for (int dc = 0; dc < DC; ++dc) o[dc][rt] *= alpha;
+      }
+      const float mb = m_ref[rt] == -INFINITY ? 0.f : -m_ref[rt] * sl2;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      mx = fmaxf(mx, fmaxf(fmaxf(sacc[j][0], sacc[j][1]), fmaxf(sacc[j][2], sacc[j][3])));
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (__ballot(mx > m_ref + slack) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < DCW; ++c) o[c] *= alpha;
-    }
-    uint2 pb[NJ];  // P^T B operands: keys 16 j + 4 grp .. + 3 of row 16 rh + l16
-    {
-      const float mb = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < 2; ++j) {
         float e[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          e[r] = fast_exp2(fmaf(sacc[j][r], sl2, mb));
-          l_run += e[r];
+          e[r] = fast_exp2(fmaf(sacc[j][rt][r], sl2, mb));
+          l_run[rt] += e[r];
         }
-        pb[j] = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
+        pb[j][rt] = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
       }
     }
 
-    // ---- O^T += V^T P^T for this wave's head dims: lane (grp, l16) addresses
-    // key 16 j + 4 grp + l16/4, dims 16 dc + 4 (l16 % 4) .. + 3, and receives
-    // V[4 keys][16 dc + l16]
+    // ---- O^T += V^T P^T: lane (grp, l16) addresses key 16 j + 4 grp + l16/4,
+    // dims 16 dc + 4 (l16 % 4) .. + 3, and receives V[4 keys][16 dc + l16]
     {
-      const char* vb = (const char*)&s_v[buf][0];
+      const char* vb = (const char*)slot;
 #pragma unroll
-      for (int c = 0; c < DCW; ++c) {
-        const int d = 16 * (dg * DCW + c) + 4 * (l16 & 3);
+      for (int dc = 0; dc < DC; ++dc) {
+        const int d = 16 * dc + 4 * (l16 & 3);
         const int lp = d >> 3;
         const int within = (d & 4) ? 8 : 0;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int kr = (16 * j + 4 * grp + (l16 >> 2)) * HP + hh;  // tile row of the key for this head
+        for (int j = 0; j < 2; ++j) {
+          const int kr = 16 * j + 4 * grp + (l16 >> 2);
           const uint2 x = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
-          o[c] = mfma16_k16(x, pb[j], o[c]);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) o[dc][rt] = mfma16_k16(x, pb[j][rt], o[dc][rt]);
         }
       }
     }
-
-    // tiles issued after t + 1: min(kVStages - 2, ntiles - 2 - t)
-    wait_next<kVStages, NDMA>(min(kVStages - 2, ntiles - 2 - t));
-    __syncthreads();
+    asm volatile("" ::: "memory");  // and before the next chunk's stores
   }
 
-  // ---- write this wave's columns of its valid rows
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
-  const int row = rh * 16 + l16;
-  const int i = row / G, h = row % G;
-  if (i >= nq) return;
-  const bool seen = m_ref != -INFINITY;  // false: no key of this piece is visible to the row
-  const float inv = seen ? 1.f / l_run : 0.f;
-  const int64_t head = (int64_t)g * G + h;
-  if (ns == 1) {
-    uint16_t* op = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + head) * D;
+  // ---- merge the WPH waves of each head: reference maxima and sums per row,
+  // then each wave sums its share of the O^T tiles
 #pragma unroll
-    for (int c = 0; c < DCW; ++c) {
-      const int d = 16 * (dg * DCW + c) + 4 * grp;
-      *(uint2*)(op + d) = make_uint2(pack_bf16x2(o[c][0] * inv, o[c][1] * inv),
-                                     pack_bf16x2(o[c][2] * inv, o[c][3] * inv));
+  for (int rt = 0; rt < 2; ++rt) {
+    l_run[rt] += shfl_xor_f(l_run[rt], 16);
+    l_run[rt] += shfl_xor_f(l_run[rt], 32);
+    if (grp == 0) {
+      s_m[wave][rt * 16 + l16] = m_ref[rt];
+      s_l[wave][rt * 16 + l16] = l_run[rt];
     }
-  } else {
-    const int64_t wr = (((int64_t)b * p.max_q_len + i) * p.num_q_heads + head) * p.max_splits + s;
-    float* op = p.o_part + wr * D;
+  }
+  {
+    f32x4_t* ob = (f32x4_t*)kslot;  // the whole slot, K and V parts
 #pragma unroll
-    for (int c = 0; c < DCW; ++c) {
-      const int d = 16 * (dg * DCW + c) + 4 * grp;
-      *(float4*)(op + d) = make_float4(o[c][0] * inv, o[c][1] * inv, o[c][2] * inv, o[c][3] * inv);
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) ob[(dc * 2 + rt) * 64 + lane] = o[dc][rt];
+  }
+  __syncthreads();
+
+  float M[2], inv[2], lse[2], wgt[2][WPH];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = rt * 16 + l16;
+    float mw[WPH];
+    M[rt] = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WPH; ++w) {
+      mw[w] = s_m[hh * WPH + w][row];
+      M[rt] = fmaxf(M[rt], mw[w]);
     }
-    if (dg == 0 && grp == 0) p.lse[wr] = seen ? m_ref * sl2 + __log2f(l_run) : -INFINITY;
+    float Lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPH; ++w) {
+      wgt[rt][w] = mw[w] == -INFINITY ? 0.f : fast_exp2((mw[w] - M[rt]) * sl2);
+      Lt += wgt[rt][w] * s_l[hh * WPH + w][row];
+    }
+    const bool seen = M[rt] != -INFINITY;  // false: no key of this piece is visible to the row
+    inv[rt] = seen ? 1.f / Lt : 0.f;
+    lse[rt] = seen ? M[rt] * sl2 + __log2f(Lt) : -INFINITY;
+  }
+
+  // tiles bi = 2 dc + rt with bi mod WPH == sw
+  const int64_t head0 = (int64_t)g * G;
+#pragma unroll
+  for (int bi = 0; bi < 2 * DC; ++bi) {
+    if (bi % WPH != sw) continue;  // wave-uniform
+    const int dc = bi >> 1, rt = bi & 1;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < WPH; ++w) acc += wgt[rt][w] * ((const f32x4_t*)&s_buf[hh * WPH + w][0])[bi * 64 + lane];
+    const int row = rt * 16 + l16;
+    const int i = row / G, h = row % G;
+    if (i >= nq) continue;
+    const int d = 16 * dc + 4 * grp;
+    const float iv = inv[rt];
+    if (ns == 1) {
+      uint16_t* op = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + head0 + h) * D;
+      *(uint2*)(op + d) = make_uint2(pack_bf16x2(acc[0] * iv, acc[1] * iv), pack_bf16x2(acc[2] * iv, acc[3] * iv));
+    } else {
+      const int64_t wr = (((int64_t)b * p.max_q_len + i) * p.num_q_heads + head0 + h) * p.max_splits + s;
+      *(float4*)(p.o_part + wr * D + d) = make_float4(acc[0] * iv, acc[1] * iv, acc[2] * iv, acc[3] * iv);
+      if (dc == 0 && grp == 0) p.lse[wr] = lse[rt];
+    }
   }
 }
 
@@ -388,13 +449,9 @@ __global__ __launch_bounds__(256) void verify_combine_kernel(const VerifyArgs p)
   for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(o[e]);
 }
 
-#ifndef PA_VERIFY_HEAD_PAIRS
-#define PA_VERIFY_HEAD_PAIRS 1
-#endif
-
 template <int D, int G>
 hipError_t launch_g(const VerifyArgs& a, hipStream_t stream) {
-  const bool pairs = PA_VERIFY_HEAD_PAIRS && a.num_kv_heads % 2 == 0;
+  const bool pairs = a.num_kv_heads % 2 == 0;
   const int64_t blocks = (int64_t)a.num_seqs * (a.num_kv_heads / (pairs ? 2 : 1)) * a.max_splits;
   if (blocks == 0) return hipSuccess;
   if (pairs)

@@ -13,9 +13,9 @@
 //  * The n rows x G query heads of (b, g) (at most 32, row = i G + h) are
 //    the N dimension of two 16-row matrix-core tiles, so each K/V byte is
 //    read once for all of them: S^T = K Q^T with v_mfma_f32_16x16x32_bf16,
-//    O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand (keys x
-//    rows) is exactly the score accumulator's layout, so P never leaves
-//    registers.
+//    and O^T += V^T P^T with the same instruction over a chunk's 32 keys,
+//    whose B operand (keys x rows) is the two score tiles' accumulators side
+//    by side, so P never leaves registers.
 //  * Each wave streams its own 32-key chunks of the piece (chunk c to wave
 //    c mod W of the head's W waves) with its own online softmax; the W
 //    partial results of a head are merged through LDS at the end, so the key
@@ -45,10 +45,6 @@ constexpr float kSlack = 8.0f;  // log2 units: rescale only when the maximum gro
 __device__ __forceinline__ f32x4_t mfma16_k32(const uint4& a, const uint4& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                  c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma16_k16(const uint2& a, const uint2& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
-                                                   c, 0, 0, 0);
 }
 
 // Longest-first work order for batches of at most 64 requests: position
@@ -309,13 +305,18 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(const VerifyArgs p)
         const int d = 16 * dc + 4 * (l16 & 3);
         const int lp = d >> 3;
         const int within = (d & 4) ? 8 : 0;
+        uint2 x[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int kr = 16 * j + 4 * grp + (l16 >> 2);
-          const uint2 x = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) o[dc][rt] = mfma16_k16(x, pb[j][rt], o[dc][rt]);
+          x[j] = lds_read_tr16(vb + (kr * PPR + (lp ^ v_swz<D>(kr))) * 16 + within);
         }
+        // one 32-key product: k-elements 0..3 of lane group grp are keys
+        // 4 grp + r, 4..7 keys 16 + 4 grp + r, in A and in B alike
+        const uint4 a = make_uint4(x[0].x, x[0].y, x[1].x, x[1].y);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          o[dc][rt] = mfma16_k32(a, make_uint4(pb[0][rt].x, pb[0][rt].y, pb[1][rt].x, pb[1][rt].y), o[dc][rt]);
       }
     }
     asm volatile("" ::: "memory");  // and before the next chunk's stores

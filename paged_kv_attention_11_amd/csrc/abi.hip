@@ -55,6 +55,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 #ifndef PA_DECODE_CACHED_PIECES
 #define PA_DECODE_CACHED_PIECES 1
 #endif
+#ifndef PA_PLAN_XCD_CLASSES
+#define PA_PLAN_XCD_CLASSES 1
+#endif
 
 // Automatic split plan: the longest piece (a multiple of 64, at most
 // kMaxSplitTokens for decode, kVerifyMaxSplit for verify) that still gives
@@ -251,6 +254,17 @@ pa::PlanArgs plan_args(const pa::DecodeArgs& a) {
   p.split_tokens = a.split_tokens;
   p.max_splits = a.max_splits;
   p.always_partial = a.always_partial;
+  // Request ranges whose full pieces each go to one XCD per head block (see
+  // the work order): every neighbouring request reads pages it shares with
+  // others through one L2.  Not for a cascade's own keys, which share none.
+  const int nb = a.num_kv_heads / a.heads_per_block;
+  int g = 8, x = nb;
+  while (x) {
+    const int t = g % x;
+    g = x;
+    x = t;
+  }
+  p.xcd_classes = PA_PLAN_XCD_CLASSES && !a.key_begin ? 8 / g : 1;
   return p;
 }
 

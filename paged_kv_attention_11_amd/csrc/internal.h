@@ -70,6 +70,7 @@ struct PlanArgs {
   int32_t split_tokens;
   int32_t max_splits;
   int32_t always_partial;
+  int32_t xcd_classes;  // 1 .. 8: contiguous request ranges whose full pieces are interleaved (1: request order)
 };
 
 struct DecodeArgs {

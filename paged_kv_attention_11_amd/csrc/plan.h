@@ -18,6 +18,15 @@
 // (log-uniform lengths) moved 5.44 TB/s with the pieces in grid order among
 // the empty work-groups, 5.61 TB/s with only the existing pieces in the same
 // order, and 5.88 TB/s with the full pieces first.
+//
+// With C = xcd_classes > 1 the batch is cut into C contiguous request ranges
+// and their full pieces are interleaved (entry k C + c is the k-th full piece
+// of range c while every range has one; a range that runs out drops out of
+// the rotation).  Entry i of head block gb runs on XCD (i NB + gb) mod 8, so
+// with C = 8 / gcd(NB, 8) every full piece of range c for head block gb runs
+// on one XCD, and neighbouring requests -- those a radix cache hands out
+// together, which share their prefix pages -- read those pages through one
+// L2 instead of several.
 #pragma once
 
 #include "internal.h"
@@ -37,10 +46,14 @@ __device__ __forceinline__ void build_decode_plan(const PlanArgs& p) {
   __shared__ int s_wcnt[kWaves][kPlanClasses];
   __shared__ int s_base[kPlanClasses];  // next free entry of each class
   __shared__ int s_full;                // next free entry of the full pieces
+  __shared__ int s_ct[8];               // full pieces of each request range
+  __shared__ int s_cb[8];               // full pieces of the ranges before it
   __shared__ int s_total;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = p.split_tokens, S = p.max_splits, B = p.num_seqs;
+  const int C = p.xcd_classes;
+  auto range_of = [&](int b) { return (int)((int64_t)b * C / B); };
   const uint64_t below = (1ull << lane) - 1;
 
   auto incl_scan = [&](int x) {  // inclusive prefix sum over the wave
@@ -80,6 +93,7 @@ __device__ __forceinline__ void build_decode_plan(const PlanArgs& p) {
   // kept in registers for pass 2 (a batch of at most kThreads requests is
   // read once).
   if (tid < kPlanClasses) s_base[tid] = 0;
+  if (tid < 8) s_ct[tid] = 0;
   if (tid == 0) s_full = 0;
   const Req first = info(tid);
   __syncthreads();
@@ -87,6 +101,7 @@ __device__ __forceinline__ void build_decode_plan(const PlanArgs& p) {
     const Req r = b0 == 0 ? first : info(b0 + tid);
     const int nf = incl_scan(r.nfull);
     if (lane == 63 && nf) atomicAdd(&s_full, nf);
+    if (C > 1 && r.nfull > 0) atomicAdd(&s_ct[range_of(b0 + tid)], r.nfull);
     for (int c = 1; c < kPlanClasses; ++c) {
       const int n = __popcll(__ballot(r.cls == c));
       if (lane == 0 && n) atomicAdd(&s_base[c], n);
@@ -104,6 +119,11 @@ __device__ __forceinline__ void build_decode_plan(const PlanArgs& p) {
     s_base[kPlanZero] = next;
     s_total = next + nz;
     s_full = 0;
+    int e = 0;
+    for (int c = 0; c < C; ++c) {
+      s_cb[c] = e;
+      e += s_ct[c];
+    }
   }
   __syncthreads();
 
@@ -129,7 +149,18 @@ __device__ __forceinline__ void build_decode_plan(const PlanArgs& p) {
       if (r.cls) cpos += s_wcnt[w][r.cls];
     }
     const int flag = r.single ? kPlanSingle : 0;
-    for (int s = 0; s < r.nfull; ++s) plan[fpos + s] = make_int4(b, s | flag, r.k0 + s * split, split);
+    if (C > 1) {
+      // fpos - s_cb[c]: the request's first full piece within its range
+      const int c = r.nfull > 0 ? range_of(b) : 0;
+      for (int s = 0; s < r.nfull; ++s) {
+        const int k = fpos + s - s_cb[c];
+        int pos = 0;
+        for (int c2 = 0; c2 < C; ++c2) pos += min(s_ct[c2], k) + (c2 < c && s_ct[c2] > k ? 1 : 0);
+        plan[pos] = make_int4(b, s | flag, r.k0 + s * split, split);
+      }
+    } else {
+      for (int s = 0; s < r.nfull; ++s) plan[fpos + s] = make_int4(b, s | flag, r.k0 + s * split, split);
+    }
     if (r.cls == kPlanZero) {
       plan[cpos] = make_int4(b, 0, 0, 0);
     } else if (r.cls) {

@@ -59,6 +59,38 @@ def test_large_decode_batch_matches_oracle(B, hi):
     assert bits(out_sub) == bits(out[seqs])
 
 
+@pytest.mark.parametrize("B,hkv,hq,hi,split", [
+    (997, 4, 16, 300, 64),      # one block of four KV heads: eight request ranges, 997 = 8 * 124 + 5
+    (403, 8, 32, 2200, 1024),   # two heads per block, four blocks: two ranges of 201 and 202 requests
+    (5, 4, 8, 20000, 64),       # fewer requests than ranges: some ranges hold none
+])
+def test_decode_request_ranges_match_oracle(B, hkv, hq, hi, split):
+    """The work order cuts the batch into 8 / gcd(head blocks, 8) contiguous
+    request ranges and interleaves their full pieces (so that each range's
+    pieces of a head block run on one XCD); uneven and empty ranges included.
+    Checked against the oracle and bit for bit against the same requests in
+    plain grid order."""
+    lens = lengths(B, hi, seed=B + hkv)
+    lens[0] = hi  # sets the grid
+    D = 64 if hkv == 4 else 128
+    banner(f"decode B={B} kv heads {hkv} q heads {hq} lengths<= {hi} split {split}")
+    wl = W.make_custom(lens, hq, hkv, D, 16, dtype="bf16", seed=2000 + B)
+    S = (wl.max_seq_len + split - 1) // split
+    assert B * hkv * S >= 6144  # the work order is used
+    dw = fresh(wl)
+    out = gpu_decode(wl, dw, split=split)
+    kp, vp = stored_oracle_pools(wl)
+    ref = oracle.decode(wl.q, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+    err = assert_close(f64(out), ref, f"decode ranges B={B}")
+    print(f"[result] max abs err {err:.3g}", flush=True)
+
+    seqs = [0, 3] if B < 13 else list(range(0, B, 13))
+    sub = wl.subset(seqs)
+    assert len(seqs) * hkv * ((sub.max_seq_len + split - 1) // split) < 6144
+    out_sub = gpu_decode(sub, fresh(sub), split=split)
+    assert bits(out_sub) == bits(out[seqs])
+
+
 def test_large_mixed_batch_matches_oracle():
     """Decode requests next to short chunks: the work order lists only the
     one-row requests."""

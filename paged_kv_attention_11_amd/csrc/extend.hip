@@ -662,6 +662,7 @@ template <int D>
 __global__ __launch_bounds__(256) void extend_combine_kernel(const ExtendArgs p) {
   constexpr int EPL = D / 64;
   constexpr int BATCH = 8;
+  constexpr int kFew = 8;  // rows of at most this many pieces take the one-round-trip path
   const int lane = threadIdx.x & 63;
   const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t rows = (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads;
@@ -678,6 +679,44 @@ __global__ __launch_bounds__(256) void extend_combine_kernel(const ExtendArgs p)
   const int64_t wrow = ((int64_t)(r0 + i) * p.num_q_heads + hq) * p.num_pieces;  // the row's pieces
   const float* lse = p.lse + wrow;
   const float* op = p.o_part + wrow * D + lane * EPL;
+  uint16_t* out = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + hq) * D + lane * EPL;
+
+  if (ns > 0 && ns <= kFew) {
+    // every load issued at once: the log-sum-exps (lane k: piece k) and the
+    // partial outputs do not depend on each other, so the merge waits for
+    // one memory round trip instead of two.  Same order of operations as
+    // the general path below.
+    const float l = lane < ns ? lse[lane] : -INFINITY;
+    float v[kFew][EPL];
+#pragma unroll
+    for (int k = 0; k < kFew; ++k) {
+      if (k < ns) {  // uniform
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[k][e] = op[(int64_t)k * D + e];
+      }
+    }
+    const float M = wave_max(l);
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+    if (M != -INFINITY) {
+      const float w = (lane < ns && l != -INFINITY) ? fast_exp2(l - M) : 0.f;
+      const float wsum = wave_sum(w);
+#pragma unroll
+      for (int k = 0; k < kFew; ++k) {
+        if (k < ns) {  // uniform
+          const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = wk > 0.f ? fmaf(wk, v[k][e], o[e]) : o[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] /= wsum;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(o[e]);
+    return;
+  }
 
   float M = -INFINITY;
   for (int c = 0; c < ns; c += 64) M = fmaxf(M, lse[min(c + lane, ns - 1)]);
@@ -712,7 +751,6 @@ __global__ __launch_bounds__(256) void extend_combine_kernel(const ExtendArgs p)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] /= wsum;
   }
-  uint16_t* out = (uint16_t*)p.out + ((int64_t)(r0 + i) * p.num_q_heads + hq) * D + lane * EPL;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) out[e] = (uint16_t)f32_to_bf16_bits(o[e]);
 }

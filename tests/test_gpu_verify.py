@@ -39,6 +39,8 @@ VERIFY_SWEEP = [
     ([1500, 70], [5, 5], 12, 2, 128, 1, 256),                                   # group 6, page size 1
     ([800, 50, 3100], [6, 6, 2], 12, 3, 128, 16, 0),                            # odd KV heads: one per work-group
     ([400, 2000], [3, 4], 8, 1, 64, 16, 256),                                   # one KV head, group 8, D = 64
+    ([1018, 2042, 58, 4090], [6, 6, 6, 6], 32, 8, 128, 16, 1024),              # lengths 1024, 2048, 64, 4096: no short last piece
+    ([1018, 2042, 58, 4090], [6, 6, 6, 6], 32, 8, 128, 16, 64),                # the same in 64-key pieces
 ]
 
 
@@ -54,6 +56,24 @@ def test_verify_sweep(case):
     ref = oracle.extend(wl.q, wl.q_indptr, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
     assert_close(out, ref, f"verify sweep {case}")
     assert_close(out, f64(gpu_extend(wl, dw)), f"verify sweep {case} vs extend")
+
+
+def test_verify_more_than_64_requests():
+    """Batches of more than 64 requests take the plain piece order (piece
+    index slowest, every request), not the longest-first one."""
+    rng = np.random.default_rng(731)
+    B = 70
+    n = [int(x) for x in rng.integers(1, 7, B)]
+    lens = [int(p) + k for p, k in zip(rng.integers(0, 2500, B), n)]
+    banner(f"verify B={B} lengths<= {max(lens)}")
+    for Hq, Hkv in ((32, 8), (12, 3)):
+        wl = W.make_custom(lens, Hq, Hkv, 128, 16, dtype="bf16", kind="extend", n_new=n, seed=732 + Hkv)
+        dw = fresh(wl)
+        out = f64(gpu_verify(wl, dw, 512))
+        kp, vp = stored_oracle_pools(wl)
+        ref = oracle.extend(wl.q, wl.q_indptr, kp, vp, wl.page_table, wl.seq_lens, wl.scale, wl.dtype)
+        err = assert_close(out, ref, f"verify B={B} Hkv={Hkv}")
+        print(f"[result] Hkv={Hkv} max abs err {err:.3g}", flush=True)
 
 
 def test_verify_padding_requests_and_bound_above_the_chunks():

@@ -440,17 +440,20 @@ pa_status pa_decode_cascade_order(const pa_kv_pool* pool, const void* q, int32_t
  * pa_verify: the result of pa_extend (same arguments and semantics) for
  * requests whose chunks are short, as in the verification of drafted tokens:
  * max_q_len * (num_q_heads / num_kv_heads) <= 32.  The keys of each request
- * are split into pieces of split_tokens keys (0 = the automatic choice, as
- * pa_decode_split_tokens' at one KV head per unit but at most 1024; else a
- * multiple of 64 in [64, 1024]) handled by separate
- * work-groups, each reading a K/V tile once for all rows of the chunk and all
- * query heads of a KV head; a second kernel merges the pieces.
+ * are split into pieces handled by separate work-groups, each reading its
+ * keys once for all rows of the chunk and all query heads of a KV head; a
+ * second kernel merges the pieces.
+ *   split_tokens: keys per piece (the last piece of a request shorter), a
+ *              multiple of 64 in [64, 2048]; 0: the automatic choice, 1536,
+ *              or max_seq_len rounded up to a multiple of 64 when that is
+ *              smaller (one piece per request).
  *   workspace: pa_verify_workspace_bytes(...) bytes, 256-byte aligned
  *              (0 bytes and NULL allowed when one piece covers max_seq_len).
  *              Layout: fp32 partial outputs [num_seqs, max_q_len,
  *              num_q_heads, S, head_dim], then (256-byte aligned) fp32
  *              log2-sum-exp [num_seqs, max_q_len, num_q_heads, S],
- *              S = ceil(max_seq_len / split_tokens).
+ *              S = ceil(max_seq_len / split), split = split_tokens or the
+ *              automatic choice.
  * Chunks longer than max_q_len are a contract violation (their extra rows
  * are not computed).  bf16 pools only, head_dim 128 or 64, group size
  * 1 .. 8.  Softmax weights are rounded to bf16 before the weighted sum of V.

@@ -157,6 +157,30 @@ int32_t resolve_decode_split(int32_t split_tokens, int32_t num_seqs, int32_t num
                        decode_heads_per_block(0, num_seqs, num_kv_heads, max_seq_len));
 }
 
+// The verify split: pieces of split_tokens keys (a multiple of 64 in [64,
+// kVerifyMaxSplit]), or automatically (0) of kVerifyAutoSplit keys, one
+// piece when every request is shorter.  Each verify work-group streams its
+// keys at about the same rate however many share the chip, so fewer, longer
+// pieces -- fewer partials to write and merge, fewer work-groups to set up --
+// are faster until the work-groups no longer fill the chip.  Measured on one
+// MI355X (us per call, 32/8 heads, D = 128, 6 rows per request; pieces of
+// 256 / 512 / 1024 / 1536 / 2048 keys): 64 requests of 2048 keys 139 / 116 /
+// 102 / 97 / 105; 32 of 8192 keys 258 / 218 / 196 / 189 / 175; 256 of 1030
+// keys 276 / 240 / 216 / 178 / 177; 16 of 512..16384 log-uniform 116 / 80 /
+// 77 / 71 / 67; 48 of 256..8192 log-uniform 145 / 100 / 84 / 85 / 87; 128 of
+// 706 keys 96 / 85 / 63 / 65 / 64; the Qwen3-8B-shaped verify workload 134
+// at 1024, 124-127 at 1536, 130 at 2048.  Pieces of equal length within a
+// request (ceil(L / 2048) of them, no short last piece) were slower on the
+// verify workload (129-132 us) and on four of the six batches above.
+constexpr int32_t kVerifyAutoSplit = 1536;
+int32_t resolve_verify_split(int32_t split_tokens, int32_t max_seq_len) {
+  if (split_tokens == 0) {
+    const int64_t one = ((int64_t)(max_seq_len > 0 ? max_seq_len : 1) + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
+    return (int32_t)(one < kVerifyAutoSplit ? one : kVerifyAutoSplit);
+  }
+  return resolve_split(split_tokens, 0, 1, max_seq_len, pa::kVerifyMaxSplit);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Work order of the decode partial kernel (a plan kernel lists the pieces
@@ -815,7 +839,7 @@ size_t pa_verify_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t nu
                                  int32_t head_dim, int32_t max_seq_len, int32_t split_tokens) {
   if (num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
     return 0;
-  const int32_t split = resolve_split(split_tokens, num_seqs, num_kv_heads, max_seq_len, pa::kVerifyMaxSplit);
+  const int32_t split = resolve_verify_split(split_tokens, max_seq_len);
   if (split < 0) return 0;
   const int64_t S = (max_seq_len + split - 1) / split;
   const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * (S > 1 ? S : 0);
@@ -837,7 +861,7 @@ pa_status pa_verify(const pa_kv_pool* pool, const void* q, int32_t num_q_heads, 
   if ((int64_t)max_q_len * G > 32) return PA_ERR_UNSUPPORTED;  // rows of one matrix-core tile pair
   if (max_q_len > max_seq_len) return PA_ERR_SHAPE;
   if ((int64_t)pt_stride * pool->page_size < max_seq_len) return PA_ERR_SHAPE;
-  const int32_t split = resolve_split(split_tokens, num_seqs, pool->num_kv_heads, max_seq_len, pa::kVerifyMaxSplit);
+  const int32_t split = resolve_verify_split(split_tokens, max_seq_len);
   if (split < 0) return PA_ERR_SHAPE;
   const int64_t S = (max_seq_len + split - 1) / split;
   if ((int64_t)num_seqs * pool->num_kv_heads * S > (int64_t)INT_MAX) return PA_ERR_SHAPE;

@@ -13,7 +13,7 @@ constexpr int kDecodeWaves = 4;           // waves per decode work-group
 constexpr int kDecodeTokPerIter = 16;     // keys one wave handles per iteration
 constexpr int kSplitQuantum = kDecodeWaves * kDecodeTokPerIter;  // 64
 constexpr int kMaxSplitTokens = 2048;     // decode: LDS slot staging bound
-constexpr int kVerifyMaxSplit = 1024;     // verify: page ids of a piece staged in LDS
+constexpr int kVerifyMaxSplit = 2048;     // verify: longest piece (its page ids are staged in LDS)
 constexpr int kMaxGroup = 8;              // query heads per KV head (decode)
 
 struct StoreArgs {
@@ -162,7 +162,7 @@ struct VerifyArgs {
   int32_t head_dim;
   int32_t log2_page;
   int32_t max_q_len;           // rows per request; max_q_len * G <= 32
-  int32_t split_tokens;        // keys per piece, multiple of 64, <= 1024
+  int32_t split_tokens;        // keys per piece, multiple of 64, <= kVerifyMaxSplit
   int32_t max_splits;
   float scale_log2;
 };

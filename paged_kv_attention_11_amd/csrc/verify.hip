@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(const VerifyArgs p)
   static_assert(SLOT * 16 == 32 * D * 4, "slot holds a wave's O^T");
 
   __shared__ uint4 s_buf[kThreads / 64][SLOT];
-  __shared__ int32_t s_pages[kPageCap];
+  __shared__ int32_t s_pages[kVerifyMaxSplit];  // a piece's page ids (one key per page at page size 1)
   __shared__ float s_m[kThreads / 64][32];
   __shared__ float s_l[kThreads / 64][32];
 
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(const VerifyArgs p)
       qreg[rt][ks] = __builtin_bit_cast(uint4, v);
     }
 
-  // ---- page ids of the piece (at most 1024 keys: at most 1024 pages)
+  // ---- page ids of the piece (at most kVerifyMaxSplit keys, so pages)
   const int sh = p.log2_page;
   const int pmask = (1 << sh) - 1;
   const int pg0 = k_begin >> sh;

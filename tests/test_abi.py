@@ -382,12 +382,13 @@ def test_verify_validation():
     assert verify(p, qmax=-1) == SHAPE
     assert verify(p, stride=10) == SHAPE
     assert verify(p, split=100) == SHAPE
-    assert verify(p, split=2048) == SHAPE  # verify pieces hold at most 1024 keys
+    assert verify(p, split=2112) == SHAPE  # verify pieces hold at most 2048 keys
     assert verify(p, q=0) == NULL
     assert verify(p, qi=0) == NULL
     assert verify(p, out=FAKE + 4) == SHAPE
-    assert verify(p, ws=0) == WS
-    assert verify(p, ws_bytes=4096) == WS
+    # 5000 keys: more than one automatic piece, so a workspace is needed
+    assert verify(p, ws=0, Lmax=5000, stride=400) == WS
+    assert verify(p, ws_bytes=4096, Lmax=5000, stride=400) == WS
     assert verify(p, B=0) == OK and verify(p, qmax=0) == OK
 
 
@@ -398,6 +399,13 @@ def test_verify_workspace_size():
     expect = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 8192, 1024) == expect
     assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 1000, 1024) == 0  # one piece: no workspace
+    # automatic: 1536-key pieces (6 over 8192 keys), one piece up to 1536 keys
+    for split, pieces in ((0, 6), (1536, 6), (2048, 4)):
+        rows = 64 * 6 * 32 * pieces
+        expect = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+        assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 8192, split) == expect
+    assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 1536, 0) == 0
+    assert lib.pa_verify_workspace_bytes(64, 6, 32, 8, 128, 8192, 2112) == 0  # invalid split
 
 
 def test_check_batch_validation():

@@ -41,6 +41,9 @@ VERIFY_SWEEP = [
     ([400, 2000], [3, 4], 8, 1, 64, 16, 256),                                   # one KV head, group 8, D = 64
     ([1018, 2042, 58, 4090], [6, 6, 6, 6], 32, 8, 128, 16, 1024),              # lengths 1024, 2048, 64, 4096: no short last piece
     ([1018, 2042, 58, 4090], [6, 6, 6, 6], 32, 8, 128, 16, 64),                # the same in 64-key pieces
+    ([2043, 6139, 3066, 100], [6, 6, 6, 6], 32, 8, 128, 16, 0),                # automatic 1536-key pieces: 2049, 6145 and 3072 keys
+    ([5000, 300], [4, 4], 16, 8, 64, 1, 0),                                     # page size 1: 1536 page ids per piece
+    ([5000, 300], [4, 4], 16, 8, 64, 1, 2048),                                  # page size 1, 2048-key pieces: 2048 page ids
 ]
 
 
